@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the libwkv hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one wkv_forward over the workload (B=8, T=8192, C=2048 float32 by
+default: the long-context, 1.5B-width forward).  The timed region holds K steps
+with inputs resident in HBM, bracketed by torch.cuda.synchronize().  Prints one
+JSON line: elements/s (B*T*C per second), the HBM roofline of the forward kernel
+(algorithmic bytes: read k, v, write y) measured with HIP events on the launch
+stream, and the float64 CPU oracle timed on the host as a reported baseline.
+The other workloads (169M width, 64K-token bf16, batched decode step) are timed
+the same way and reported under "other_workloads".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_device.h", "libwkv_api.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rwkv_linear_attention_libwkv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    """Run fn warmup times, then time `steps` calls with HIP events; returns (total_s, per_call_s)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = start.elapsed_time(end) / 1e3
+    return wall, ev / steps
+
+
+def forward_case(spec, steps, warmup, gen="numpy"):
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    if gen == "numpy":
+        inp = workloads.forward_inputs(spec)
+        w = torch.from_numpy(inp["w"]).cuda()
+        u = torch.from_numpy(inp["u"]).cuda()
+        k = torch.from_numpy(inp["k"]).cuda().to(dt)
+        v = torch.from_numpy(inp["v"]).cuda().to(dt)
+    else:  # same distributions drawn on the device (faster for the largest tensors)
+        rng = np.random.default_rng(spec.seed)
+        w_np, u_np = workloads.channel_params(rng, (spec.C,), spec.w_raw_lo, spec.w_raw_hi, spec.u_std)
+        w, u = torch.from_numpy(w_np).cuda(), torch.from_numpy(u_np).cuda()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(spec.seed)
+        shape = (spec.B, spec.T, spec.C)
+        k = (torch.randn(shape, generator=g, device="cuda") * spec.k_std).to(dt)
+        v = (torch.randn(shape, generator=g, device="cuda") * spec.v_std).to(dt)
+    y = torch.empty_like(k)
+    need = libwkv.wkv_forward_workspace_bytes(spec.B, spec.T, spec.C, dt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        libwkv.wkv_forward(w, u, k, v, y=y, workspace=ws)
+
+    wall, per_call = time_launches(fn, steps, warmup)
+    if need:
+        assert libwkv.lookback_error(ws) == 0, "look-back gave up"
+    elt = 4 if spec.dtype == "f32" else 2
+    bytes_per_launch = 3 * elt * spec.elements  # read k, v; write y
+    out = {
+        "workload": spec.name,
+        "elements": spec.elements,
+        "seconds": wall,
+        "per_launch_s": per_call,
+        "elements_per_s": spec.elements / per_call,
+        "algorithmic_bytes_per_launch": bytes_per_launch,
+        "achieved_GBps": bytes_per_launch / per_call / 1e9,
+        "algo": "chunked" if need else "seq",
+    }
+    del k, v, y, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def step_case(spec, steps, warmup):
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+    w_np, u_np = workloads.step_params(spec)
+    w, u = torch.from_numpy(w_np).cuda(), torch.from_numpy(u_np).cuda()
+    a, b, p = libwkv.empty_state((spec.N, spec.G, spec.C))
+    for s in range(spec.prefix):  # the seeded prefix builds the starting state (not timed)
+        k, v = workloads.step_kv(spec, s, device="cuda")
+        libwkv.wkv_step(w, u, k, v, a, b, p)
+    kv = [workloads.step_kv(spec, spec.prefix + s, device="cuda") for s in range(spec.steps)]
+    y = torch.empty_like(kv[0][0])
+    torch.cuda.synchronize()
+
+    def one_decode():  # the 16 successive steps of the workload
+        for k, v in kv:
+            libwkv.wkv_step(w, u, k, v, a, b, p, y=y)
+
+    wall, per_call = time_launches(one_decode, max(1, steps // 4), 1)
+    lane_steps = spec.lanes * spec.steps
+    bytes_per_step = 30 * spec.lanes  # k, v 2+2, a b p 12 read + 12 written, y 2
+    out = {
+        "workload": spec.name,
+        "lane_steps": lane_steps,
+        "per_decode_s": per_call,
+        "per_step_launch_s": per_call / spec.steps,
+        "lane_steps_per_s": lane_steps / per_call,
+        "algorithmic_bytes_per_launch": bytes_per_step,
+        "achieved_GBps": bytes_per_step / (per_call / spec.steps) / 1e9,
+    }
+    del kv, a, b, p, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(spec, budget_s=20.0):
+    """The float64 oracle (wkv_recurrent) on a bounded sample of the workload, on the host."""
+    import numpy as np
+
+    from oracle import wkv_recurrent
+    from rwkv_linear_attention_libwkv_amd import workloads
+
+    inp = workloads.forward_inputs(spec)
+    # probe the cost per token, then size the sample (all lanes, leading tokens) to the budget
+    t0 = time.perf_counter()
+    wkv_recurrent(inp["w"], inp["u"], inp["k"][:, :64], inp["v"][:, :64])
+    per_token = (time.perf_counter() - t0) / 64
+    n_tok = int(min(spec.T, max(64, budget_s / max(per_token, 1e-9))))
+    t0 = time.perf_counter()
+    wkv_recurrent(inp["w"], inp["u"], inp["k"][:, :n_tok], inp["v"][:, :n_tok])
+    dt = time.perf_counter() - t0
+    elements = spec.B * n_tok * spec.C
+    return {
+        "value": elements / dt,
+        "unit": "elements/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"wkv_recurrent (float64 NumPy, one process) over all {spec.B * spec.C} lanes of "
+                  f"{spec.name}, tokens 0..{n_tok - 1}: {elements} elements in {dt:.1f} s",
+        "numpy": np.__version__,
+    }
+
+
+COPY_BYTES = 512 << 20
+
+
+def profile_run(name, launches):
+    """Launches to profile: the workload's forward (or decode step) and a plain copy."""
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import workloads
+
+    if name in workloads.FORWARD_SPECS:
+        spec = workloads.FORWARD_SPECS[name]
+        r = forward_case(spec, launches, 1, gen="torch")
+        print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch", flush=True)
+    else:
+        r = step_case(workloads.STEP_DECODE, 4, 1)
+        print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step", flush=True)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)  # reads and writes COPY_BYTES each
+    torch.cuda.synchronize()
+    print(f"# copy calibration: {COPY_BYTES} bytes read and written per launch", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wkv_fwd_f32_B8_T8192_C2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="time only the main workload")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="a few launches of the workload's kernel and of a plain 512 MiB copy "
+                         "(the byte-counter calibration), for rocprofv3")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the WKV lanes are independent, so this build "
+              "measures one GPU's share (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads  # noqa: F401  (fails loudly if unbuilt)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile_run:
+        profile_run(args.workload, max(1, min(args.steps, 5)))
+        return
+    spec = workloads.FORWARD_SPECS[args.workload]
+    main_res = forward_case(spec, args.steps, args.warmup)
+    print(f"# {spec.name}: {main_res['per_launch_s'] * 1e6:.1f} us/launch, "
+          f"{main_res['achieved_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    others = []
+    if not args.no_others:
+        for name, s in workloads.FORWARD_SPECS.items():
+            if name == spec.name or s.elements < 1e6:
+                continue
+            gen = "torch" if s.elements > 2e8 else "numpy"
+            r = forward_case(s, max(5, args.steps // 2), 2, gen=gen)
+            others.append(r)
+            print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch, {r['achieved_GBps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        r = step_case(workloads.STEP_DECODE, args.steps, 1)
+        others.append(r)
+        print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "
+              f"{r['achieved_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    bytes_per_launch = main_res["algorithmic_bytes_per_launch"]
+    achieved = main_res["achieved_GBps"]
+    traffic = measured_traffic(spec.name)
+    line = {
+        "metric": "WKV fwd elements/sec (B*T*C) and achieved HBM GB/s vs MI355X peak",
+        "value": main_res["elements_per_s"],
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["per_launch_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if spec.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded NumPy draws; no dataset or weights involved)",
+        "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "C": spec.C,
+                   "algo": main_res["algo"], "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(spec),
+        "other_workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * libwkv -- the RWKV-4 time-mixing WKV operator for AMD MI355X (gfx950).
+ *
+ * The operation (page "Reinventing RNNs for the Transformer Era: RWKV", a paper
+ * review on velog; section "WKV 연산자", WKV equation), for every batch b,
+ * channel c and time t = 1..T:
+ *
+ *   y_t = ( sum_{i<t} e^{-(t-1-i) w + k_i} v_i + e^{u + k_t} v_t )
+ *         / ( sum_{i<t} e^{-(t-1-i) w + k_i} + e^{u + k_t} )
+ *
+ * with w (the decay rate itself, applied as e^{-w}) and u (the bonus of the
+ * current token) per channel.  Section "RNN-유사추론" of the same page gives
+ * the RNN form y_t = (A_t + e^{u+k_t} v_t) / (B_t + e^{u+k_t}) with a
+ * per-channel state (A_t, B_t) carried to the next token (its decoding list,
+ * steps 4 and 7).  This library advances the state as
+ * A_{t+1} = e^{-w} A_t + e^{k_t} v_t, B_{t+1} = e^{-w} B_t + e^{k_t}, the
+ * reading that reproduces the WKV equation.
+ *
+ * State triples.  A state is stored as three float32 arrays (a, b, p) meaning
+ * A = a * e^p and B = b * e^p.  The representation is not unique: (a e^d,
+ * b e^d, p - d) is the same state, so compare log B = p + log b and A / B.
+ * The empty state (no past) is a = b = 0, p = WKV_P_EMPTY.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers on the current HIP device; the caller owns
+ *    every buffer.  Tensors are dense and row-major with the channel index
+ *    fastest: k, v, y are [B, T, C] (forward) or [N, G, C] (step).
+ *  - Calls are asynchronous on `stream` (0 = the null stream): the library
+ *    never synchronises, never allocates and keeps no state between calls.
+ *  - All argument checks happen before any HIP call.  A negative size, or a
+ *    NULL pointer for a non-empty operand, gives WKV_EINVAL; an unknown dtype
+ *    gives WKV_EDTYPE; a workspace smaller than the query gives
+ *    WKV_EWORKSPACE; a failed launch gives WKV_EHIP.  Any zero size returns
+ *    WKV_OK without touching the GPU.
+ *  - y must not alias k or v (not detected).  NaN and Inf in the inputs
+ *    propagate to the outputs; nothing traps.
+ *  - Results are bitwise reproducible for a given shape, dtype, algorithm
+ *    and chunk length.
+ */
+#ifndef LIBWKV_H
+#define LIBWKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wkv_status {
+    WKV_OK = 0,
+    WKV_EINVAL = 1,     /* bad size, NULL pointer, bad algorithm or chunk length */
+    WKV_EDTYPE = 2,     /* unknown dtype */
+    WKV_EWORKSPACE = 3, /* workspace missing or too small */
+    WKV_EHIP = 4        /* a HIP launch failed */
+} wkv_status;
+
+/* dtype of k, v and y.  w, u and the state (a, b, p) are always float32, and
+ * all arithmetic is float32 with float64 exponent bookkeeping. */
+typedef enum wkv_dtype {
+    WKV_F32 = 0,
+    WKV_BF16 = 1 /* bfloat16; y is rounded to nearest-even */
+} wkv_dtype;
+
+/* How wkv_forward_ex computes the time recurrence. */
+typedef enum wkv_algo {
+    WKV_ALGO_AUTO = 0,    /* pick by the number of lanes B*C versus T */
+    WKV_ALGO_SEQ = 1,     /* one thread walks all of T for its channels */
+    WKV_ALGO_CHUNKED = 2  /* T split into chunks, single-pass chained scan */
+} wkv_algo;
+
+/* p of the empty state (a = b = 0). */
+#define WKV_P_EMPTY (-1.0e38f)
+
+/* Chunk lengths (time steps per workgroup tile) accepted by the chunked
+ * algorithm; 0 selects the default for the dtype. */
+#define WKV_CHUNK_LENS {64, 128, 256}
+
+/*
+ * Bytes of device workspace that wkv_forward_ex needs for this problem with
+ * this algorithm and chunk length (0 for the sequential algorithm).  The same
+ * value serves wkv_forward (algo AUTO, chunk_len 0) and wkv_forward_state.
+ * Returns 0 for empty problems and (size_t)-1 for invalid arguments.
+ */
+size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                                   wkv_algo algo, int64_t chunk_len);
+
+/*
+ * Whole-sequence WKV (the page's time-parallel training mode, section
+ * "Transformer-유사학습": every op runs over batch and time at once and only
+ * WKV runs as a scan).
+ *   w, u : [C] float32 device arrays.
+ *   k, v : [B, T, C] device arrays of dtype dt (read only).
+ *   y    : [B, T, C] device array of dtype dt (written).
+ *   ws   : device workspace of at least wkv_forward_workspace_bytes(...)
+ *          bytes; its contents on entry do not matter and are overwritten.
+ *          One workspace must not be used by two calls that may run at the
+ *          same time.
+ * Starts every lane from the empty state.
+ */
+wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                       const float* w, const float* u,
+                       const void* k, const void* v, void* y,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* wkv_forward with an explicit algorithm and chunk length (0 = default). */
+wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                          const float* w, const float* u,
+                          const void* k, const void* v, void* y,
+                          void* ws, size_t ws_bytes,
+                          wkv_algo algo, int64_t chunk_len, hipStream_t stream);
+
+/*
+ * Whole-sequence WKV that starts from a given state and returns the final
+ * one: the prefill that hands over to wkv_step (the page's time-parallel mode
+ * joined to its time-sequential mode; the state after token T is the one the
+ * decoding loop stores for token T+1).
+ *   state_in_a/b/p  : [B, C] float32 device arrays, or all three NULL for the
+ *                     empty state.
+ *   state_out_a/b/p : [B, C] float32 device arrays written with the state
+ *                     after the last token, or all three NULL.  They may be
+ *                     the same arrays as state_in_*.
+ * The other arguments are those of wkv_forward_ex.  With T = 0 the state is
+ * copied through (a launch is made only when in and out differ).
+ */
+wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                             const float* w, const float* u,
+                             const void* k, const void* v, void* y,
+                             const float* state_in_a, const float* state_in_b,
+                             const float* state_in_p,
+                             float* state_out_a, float* state_out_b, float* state_out_p,
+                             void* ws, size_t ws_bytes,
+                             wkv_algo algo, int64_t chunk_len, hipStream_t stream);
+
+/*
+ * One RNN-mode decoding step for N sequences x G layer slots x C channels
+ * (section "RNN-유사추론" equation, and steps 4 and 7 of its decoding list:
+ * update the WKV state, then store it for the next token).
+ *   w, u    : [G, C] float32 device arrays (shared by the N sequences).
+ *   k, v    : [N, G, C] device arrays of dtype dt (read only).
+ *   a, b, p : [N, G, C] float32 device arrays: the state before the token on
+ *             entry, the state after it on return (updated in place).
+ *   y       : [N, G, C] device array of dtype dt (written).
+ */
+wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt,
+                    const float* w, const float* u,
+                    const void* k, const void* v,
+                    float* a, float* b, float* p,
+                    void* y, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char* wkv_status_string(wkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBWKV_H */

@@ -1,0 +1,215 @@
+// libwkv C ABI: argument checks, algorithm and tile planning, workspace carve-up and
+// launches on the caller's stream.  Every check runs before any HIP call; nothing here
+// allocates, synchronises or keeps state between calls.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <climits>
+
+#include "libwkv.h"
+#include "wkv_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kDefaultTile = 128;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool dtype_ok(wkv_dtype dt) { return dt == WKV_F32 || dt == WKV_BF16; }
+size_t dtype_size(wkv_dtype dt) { return dt == WKV_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Channels per thread of the forward kernels.  Only one channel per thread is built at
+// present: wider rows push the kernels past four waves per SIMD.
+constexpr int kFwdMaxNch = 1;
+
+// Channels per thread: 4, 2 or 1, the largest that divides C and keeps the rows aligned.
+int pick_nch(int64_t C, size_t elt, int max_nch, const void* k, const void* v, const void* y) {
+    for (int n = max_nch; n > 1; n /= 2) {
+        const size_t bytes = elt * (size_t)n;
+        if (C % n == 0 && aligned(k, bytes) && aligned(v, bytes) && aligned(y, bytes)) return n;
+    }
+    return 1;
+}
+
+bool tile_ok(int64_t t) { return t == 0 || t == 64 || t == 128 || t == 256; }
+
+// AUTO: enough (b, c) lanes to fill the chip, or a sequence shorter than one tile, walks
+// T sequentially; otherwise T is split into tiles.
+int resolve_algo(wkv_algo algo, int64_t B, int64_t T, int64_t C) {
+    if (algo != WKV_ALGO_AUTO) return (int)algo;
+    if (B > 65535) return WKV_ALGO_CHUNKED;  // the sequential grid holds batch rows in y
+    if (T <= 64 || B * C >= (int64_t)1 << 19) return WKV_ALGO_SEQ;
+    return WKV_ALGO_CHUNKED;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workspace bytes of the chunked algorithm for a given channels-per-thread choice.
+size_t chunked_bytes(int64_t B, int64_t T, int64_t C, int tile, int nch) {
+    const int64_t gw = 64 * nch;
+    const int64_t n_groups = B * ceil_div(C, gw);
+    const int64_t n_tiles = n_groups * ceil_div(T, tile);
+    return kAlign + align_up((size_t)n_tiles * 4, kAlign) + (size_t)n_tiles * 2 * 3 * gw * 4 + kAlign;
+}
+
+// Upper bound over the channels-per-thread choices the launch may make.
+size_t chunked_bytes_bound(int64_t B, int64_t T, int64_t C, int tile) {
+    size_t m = 0;
+    for (int n = 1; n <= kFwdMaxNch; n *= 2) {
+        const size_t s = chunked_bytes(B, T, C, tile, n);
+        if (s > m) m = s;
+    }
+    return m;
+}
+
+bool sizes_ok(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0) return false;
+    if (B > INT_MAX || T > INT_MAX || C > INT_MAX) return false;
+    if (B > 0 && C > 0 && B * C > INT_MAX) return false;
+    return true;
+}
+
+wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w,
+                        const float* u, const void* k, const void* v, void* y,
+                        const float* sia, const float* sib, const float* sip, float* soa,
+                        float* sob, float* sop, void* ws, size_t ws_bytes, wkv_algo algo,
+                        int64_t chunk_len, hipStream_t stream) {
+    if (!sizes_ok(B, T, C)) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return WKV_EINVAL;
+    if (!tile_ok(chunk_len)) return WKV_EINVAL;
+    const bool in_any = sia || sib || sip, in_all = sia && sib && sip;
+    const bool out_any = soa || sob || sop, out_all = soa && sob && sop;
+    if (in_any != in_all || out_any != out_all) return WKV_EINVAL;
+    if (B == 0 || C == 0) return WKV_OK;
+    if (T == 0) {
+        if (!out_all) return WKV_OK;
+        if (soa == sia && sob == sib && sop == sip) return WKV_OK;
+        return wkv::launch_copy_state(sia, sib, sip, soa, sob, sop, (long)(B * C), stream) == hipSuccess
+                   ? WKV_OK
+                   : WKV_EHIP;
+    }
+    if (!w || !u || !k || !v || !y) return WKV_EINVAL;
+
+    wkv::FwdArgs a{};
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.sin_a = sia;
+    a.sin_b = sib;
+    a.sin_p = sip;
+    a.sout_a = soa;
+    a.sout_b = sob;
+    a.sout_p = sop;
+    a.B = (int)B;
+    a.T = (int)T;
+    a.C = (int)C;
+
+    const int dtype = dt == WKV_F32 ? 0 : 1;
+    const size_t elt = dtype_size(dt);
+    const int resolved = resolve_algo(algo, B, T, C);
+    if (resolved == WKV_ALGO_SEQ) {
+        if (B > 65535) return WKV_EINVAL;  // batch rows are grid.y
+        const int nch = pick_nch(C, elt, kFwdMaxNch, k, v, y);
+        return wkv::launch_fwd_seq(a, dtype, nch, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+    }
+
+    const int tile = chunk_len ? (int)chunk_len : kDefaultTile;
+    const size_t need = chunked_bytes_bound(B, T, C, tile);
+    if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
+    const int nch = pick_nch(C, elt, kFwdMaxNch, k, v, y);
+    const int64_t gw = 64 * nch;
+    a.groups_per_row = (int)ceil_div(C, gw);
+    a.n_groups = (int)(B * a.groups_per_row);
+    a.n_chunks = (int)ceil_div(T, tile);
+    const int64_t n_tiles = (int64_t)a.n_groups * a.n_chunks;
+    if (n_tiles > INT_MAX) return WKV_EINVAL;
+    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    a.ctrl = reinterpret_cast<uint32_t*>(base);
+    a.flags = reinterpret_cast<uint32_t*>(base + kAlign);
+    a.recs = reinterpret_cast<float*>(base + kAlign + align_up((size_t)n_tiles * 4, kAlign));
+    return wkv::launch_fwd_chunked(a, dtype, nch, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt, wkv_algo algo,
+                                   int64_t chunk_len) {
+    if (!sizes_ok(B, T, C) || !dtype_ok(dt) || !tile_ok(chunk_len)) return (size_t)-1;
+    if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return (size_t)-1;
+    if (B == 0 || T == 0 || C == 0) return 0;
+    if (resolve_algo(algo, B, T, C) == WKV_ALGO_SEQ) return 0;
+    return chunked_bytes_bound(B, T, C, chunk_len ? (int)chunk_len : kDefaultTile);
+}
+
+wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                       const void* k, const void* v, void* y, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    return forward_impl(B, T, C, dt, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, ws, ws_bytes, WKV_ALGO_AUTO, 0, stream);
+}
+
+wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w,
+                          const float* u, const void* k, const void* v, void* y, void* ws,
+                          size_t ws_bytes, wkv_algo algo, int64_t chunk_len, hipStream_t stream) {
+    return forward_impl(B, T, C, dt, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, ws, ws_bytes, algo, chunk_len, stream);
+}
+
+wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w,
+                             const float* u, const void* k, const void* v, void* y,
+                             const float* state_in_a, const float* state_in_b,
+                             const float* state_in_p, float* state_out_a, float* state_out_b,
+                             float* state_out_p, void* ws, size_t ws_bytes, wkv_algo algo,
+                             int64_t chunk_len, hipStream_t stream) {
+    return forward_impl(B, T, C, dt, w, u, k, v, y, state_in_a, state_in_b, state_in_p, state_out_a,
+                        state_out_b, state_out_p, ws, ws_bytes, algo, chunk_len, stream);
+}
+
+wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                    const void* k, const void* v, float* a, float* b, float* p, void* y,
+                    hipStream_t stream) {
+    if (N < 0 || G < 0 || C < 0) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (N == 0 || G == 0 || C == 0) return WKV_OK;
+    if (G > INT_MAX || C > INT_MAX || G * C > INT_MAX) return WKV_EINVAL;
+    if (N > (int64_t)(LONG_MAX / 4) / (G * C)) return WKV_EINVAL;
+    if (!w || !u || !k || !v || !a || !b || !p || !y) return WKV_EINVAL;
+    const size_t elt = dtype_size(dt);
+    int nch = 1;
+    if (C % 4 == 0 && aligned(w, 16) && aligned(u, 16) && aligned(a, 16) && aligned(b, 16) &&
+        aligned(p, 16) && aligned(k, 4 * elt) && aligned(v, 4 * elt) && aligned(y, 4 * elt))
+        nch = 4;
+    wkv::StepArgs s{};
+    s.w = w;
+    s.u = u;
+    s.k = k;
+    s.v = v;
+    s.a = a;
+    s.b = b;
+    s.p = p;
+    s.y = y;
+    s.n_lanes = (long)(N * G * C);
+    s.GC = (int)(G * C);
+    return wkv::launch_step(s, dt == WKV_F32 ? 0 : 1, nch, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
+const char* wkv_status_string(wkv_status s) {
+    switch (s) {
+        case WKV_OK: return "WKV_OK";
+        case WKV_EINVAL: return "WKV_EINVAL: invalid size, pointer, algorithm or chunk length";
+        case WKV_EDTYPE: return "WKV_EDTYPE: unknown dtype";
+        case WKV_EWORKSPACE: return "WKV_EWORKSPACE: workspace missing or too small";
+        case WKV_EHIP: return "WKV_EHIP: a HIP launch failed";
+    }
+    return "unknown wkv_status";
+}
+
+}  // extern "C"

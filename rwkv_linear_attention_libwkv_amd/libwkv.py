@@ -1,0 +1,207 @@
+"""Python binding of libwkv (ctypes): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI declared
+in include/libwkv.h.  torch tensors serve as device memory and
+``torch.cuda.current_stream()`` as the stream; nothing here computes WKV, and
+importing this module fails loudly when libwkv.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libwkv.so")
+
+WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_EWORKSPACE, WKV_EHIP = range(5)
+WKV_F32, WKV_BF16 = 0, 1
+ALGOS = {"auto": 0, "seq": 1, "chunked": 2}
+P_EMPTY = -1.0e38
+
+#: every function include/libwkv.h declares
+EXPORTS = (
+    "wkv_forward_workspace_bytes",
+    "wkv_forward",
+    "wkv_forward_ex",
+    "wkv_forward_state",
+    "wkv_step",
+    "wkv_status_string",
+)
+
+
+class WkvError(RuntimeError):
+    """A libwkv call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m rwkv_linear_attention_libwkv_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.wkv_forward_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i64]
+    lib.wkv_forward_workspace_bytes.restype = sz
+    lib.wkv_forward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.wkv_forward.restype = i32
+    lib.wkv_forward_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, i32, i64, vp]
+    lib.wkv_forward_ex.restype = i32
+    lib.wkv_forward_state.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, vp, sz, i32, i64, vp]
+    lib.wkv_forward_state.restype = i32
+    lib.wkv_step.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.wkv_step.restype = i32
+    lib.wkv_status_string.argtypes = [i32]
+    lib.wkv_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def wkv_status_string(status: int) -> str:
+    return lib.wkv_status_string(int(status)).decode()
+
+
+status_string = wkv_status_string
+
+
+def _check(status: int, where: str):
+    if status != WKV_OK:
+        raise WkvError(status, where)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return WKV_F32
+    if t == torch.bfloat16:
+        return WKV_BF16
+    raise TypeError(f"k, v must be float32 or bfloat16, got {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def wkv_forward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32, algo: str = "auto",
+                                chunk_len: int = 0) -> int:
+    n = lib.wkv_forward_workspace_bytes(B, T, C, _dtype_code(dtype), ALGOS[algo], chunk_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid arguments for the workspace query")
+    return int(n)
+
+
+def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, workspace=None,
+                state=None, return_state: bool = False, state_out=None, stream=None):
+    """y = WKV(w, u, k, v) for k, v of shape [B, T, C] (float32 or bfloat16, on the GPU).
+
+    Calls wkv_forward_ex, or wkv_forward_state when a state goes in or out.
+
+    state: optional (a, b, p) float32 tensors of shape [B, C] to start from.
+    return_state: also return the state after the last token as (a, b, p)
+    (written into ``state_out`` when given; may be the ``state`` tensors).
+    """
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must both be [B, T, C]")
+    _need(k.is_cuda and v.is_cuda and w.is_cuda and u.is_cuda, "all tensors must be on the GPU")
+    _need(k.dtype == v.dtype, "k and v must share a dtype")
+    _need(k.is_contiguous() and v.is_contiguous(), "k and v must be contiguous")
+    B, T, C = k.shape
+    _need(w.dtype == torch.float32 and u.dtype == torch.float32, "w and u must be float32")
+    _need(w.numel() == C and u.numel() == C and w.is_contiguous() and u.is_contiguous(),
+          "w and u must be contiguous with C entries")
+    dt = _dtype_code(k.dtype)
+    if y is None:
+        y = torch.empty_like(k)
+    _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    need = wkv_forward_workspace_bytes(B, T, C, k.dtype, algo, chunk_len)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "bad workspace")
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _stream(stream)
+    if state is None and not return_state:
+        _check(lib.wkv_forward_ex(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                  ws_ptr, ws_bytes, ALGOS[algo], chunk_len, st), "wkv_forward_ex")
+        return y
+    sin = (None, None, None)
+    if state is not None:
+        sin = tuple(state)
+        for t in sin:
+            _need(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == B * C,
+                  "state tensors must be contiguous float32 with B*C entries")
+    sout = (None, None, None)
+    if return_state:
+        sout = tuple(state_out) if state_out is not None else tuple(
+            torch.empty((B, C), dtype=torch.float32, device=k.device) for _ in range(3))
+        for t in sout:
+            _need(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == B * C,
+                  "state tensors must be contiguous float32 with B*C entries")
+    _check(lib.wkv_forward_state(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                 *(_ptr(t) for t in sin), *(_ptr(t) for t in sout),
+                                 ws_ptr, ws_bytes, ALGOS[algo], chunk_len, st), "wkv_forward_state")
+    return (y, sout) if return_state else y
+
+
+def wkv_step(w, u, k, v, a, b, p, *, y=None, stream=None):
+    """One decoding step for k, v of shape [N, G, C]; (a, b, p) [N, G, C] float32 updated in place.
+
+    w, u: float32 [G, C].  Returns y (dtype of k).
+    """
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must both be [N, G, C]")
+    N, G, C = k.shape
+    _need(k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous(), "bad k or v")
+    for t in (a, b, p):
+        _need(t.shape == k.shape and t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda,
+              "a, b, p must be contiguous float32 [N, G, C]")
+    _need(w.dtype == torch.float32 and u.dtype == torch.float32, "w and u must be float32")
+    _need(w.numel() == G * C and u.numel() == G * C and w.is_contiguous() and u.is_contiguous(),
+          "w and u must be contiguous [G, C]")
+    if y is None:
+        y = torch.empty_like(k)
+    _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    _check(lib.wkv_step(N, G, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                        _ptr(a), _ptr(b), _ptr(p), _ptr(y), _stream(stream)), "wkv_step")
+    return y
+
+
+def empty_state(shape, device="cuda"):
+    """(a, b, p) float32 tensors of the empty state (a = b = 0, p = P_EMPTY)."""
+    a = torch.zeros(shape, dtype=torch.float32, device=device)
+    b = torch.zeros(shape, dtype=torch.float32, device=device)
+    p = torch.full(shape, P_EMPTY, dtype=torch.float32, device=device)
+    return a, b, p
+
+
+def lookback_error(workspace) -> int:
+    """Non-zero if a chunked call that used ``workspace`` gave up waiting in its look-back.
+
+    Reads the second control word of the workspace (after the call has finished).
+    """
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    return int(workspace[off + 4: off + 8].view(torch.int32).item())
+
+
+# short aliases
+forward = wkv_forward
+step = wkv_step
+workspace_bytes = wkv_forward_workspace_bytes

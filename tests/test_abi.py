@@ -1,0 +1,119 @@
+"""Host-side checks of the libwkv C ABI: no GPU needed.
+
+Every argument check runs before any HIP call, so invalid calls are exercised
+here with dummy pointers; nothing in this file launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libwkv.h")
+
+from rwkv_linear_attention_libwkv_amd import libwkv  # noqa: E402
+
+lib = libwkv.lib
+OK, EINVAL, EDTYPE, EWS = libwkv.WKV_OK, libwkv.WKV_EINVAL, libwkv.WKV_EDTYPE, libwkv.WKV_EWORKSPACE
+F32, BF16 = libwkv.WKV_F32, libwkv.WKV_BF16
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation or is empty
+NULL = None
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    declared = header_functions()
+    assert set(declared) == set(libwkv.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(5):
+        assert libwkv.status_string(s).startswith("WKV_")
+    assert "unknown" in libwkv.status_string(99)
+
+
+def fwd(B, T, C, dt=F32, w=P, u=P, k=P, v=P, y=P, ws=NULL, ws_bytes=0, algo=0, chunk=0):
+    return lib.wkv_forward_ex(B, T, C, dt, w, u, k, v, y, ws, ws_bytes, algo, chunk, None)
+
+
+def test_forward_argument_checks():
+    assert fwd(-1, 4, 4) == EINVAL
+    assert fwd(1, -4, 4) == EINVAL
+    assert fwd(1, 4, -4) == EINVAL
+    assert fwd(1, 4, 4, dt=7) == EDTYPE
+    assert fwd(1, 4, 4, algo=9) == EINVAL
+    assert fwd(1, 4, 4, chunk=100) == EINVAL
+    assert fwd(1, 4, 4, k=NULL) == EINVAL
+    assert fwd(1, 4, 4, y=NULL, algo=1) == EINVAL
+    assert fwd(1, 1 << 31, 4) == EINVAL
+    assert fwd(1 << 20, 4, 1 << 12) == EINVAL  # B*C beyond int32
+    # chunked needs a workspace of the queried size
+    assert fwd(2, 1000, 64, algo=2) == EWS
+    need = lib.wkv_forward_workspace_bytes(2, 1000, 64, F32, 2, 0)
+    assert need > 0
+    assert fwd(2, 1000, 64, algo=2, ws=P, ws_bytes=need - 1) == EWS
+
+
+def test_forward_empty_problems_are_noops():
+    for B, T, C in [(0, 5, 5), (5, 0, 5), (5, 5, 0)]:
+        assert fwd(B, T, C, w=NULL, u=NULL, k=NULL, v=NULL, y=NULL) == OK
+
+
+def test_forward_state_pointer_checks():
+    def st(sia, sib, sip, soa, sob, sop, T=4):
+        return lib.wkv_forward_state(1, T, 4, F32, P, P, P, P, P, sia, sib, sip, soa, sob, sop,
+                                     None, 0, 1, 0, None)
+    assert st(P, NULL, NULL, NULL, NULL, NULL) == EINVAL
+    assert st(NULL, NULL, NULL, P, P, NULL) == EINVAL
+    # T = 0 with the same arrays in and out: nothing to do
+    assert st(P, P, P, P, P, P, T=0) == OK
+    # T = 0 without state out: nothing to do
+    assert st(NULL, NULL, NULL, NULL, NULL, NULL, T=0) == OK
+
+
+def test_workspace_query():
+    q = lib.wkv_forward_workspace_bytes
+    bad = ctypes.c_size_t(-1).value
+    assert q(-1, 4, 4, F32, 0, 0) == bad
+    assert q(1, 4, 4, 5, 0, 0) == bad
+    assert q(1, 4, 4, F32, 0, 77) == bad
+    assert q(1, 4, 4, F32, 3, 0) == bad
+    assert q(0, 4, 4, F32, 2, 0) == 0
+    assert q(8, 8192, 2048, F32, 1, 0) == 0  # the sequential walk needs none
+    a = q(8, 8192, 2048, F32, 2, 0)
+    assert a > 0 and a == q(8, 8192, 2048, BF16, 2, 0)
+    assert q(8, 8192, 2048, F32, 2, 64) > q(8, 8192, 2048, F32, 2, 256)
+    # AUTO picks the chunked scan for long T with few lanes, the walk for short T
+    assert q(1, 65536, 5120, BF16, 0, 0) > 0
+    assert q(1, 64, 64, F32, 0, 0) == 0
+
+
+def test_step_argument_checks():
+    def step(N, G, C, dt=BF16, ptrs=(P,) * 8):
+        return lib.wkv_step(N, G, C, dt, *ptrs, None)
+    assert step(-1, 2, 2) == EINVAL
+    assert step(1, -2, 2) == EINVAL
+    assert step(1, 2, -2) == EINVAL
+    assert step(1, 2, 2, dt=3) == EDTYPE
+    assert step(0, 2, 2, ptrs=(NULL,) * 8) == OK
+    for i in range(8):
+        ptrs = [P] * 8
+        ptrs[i] = NULL
+        assert step(1, 2, 2, ptrs=tuple(ptrs)) == EINVAL, i
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+
+    monkeypatch.setattr(libwkv, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        libwkv._load()
+    importlib.reload(libwkv)  # restore the real module state

@@ -1,0 +1,201 @@
+"""GPU parity of wkv_forward (both algorithms) against the float64 oracle.
+
+Gate: scale-normalised error max |y_gpu - y| / s (s = the convex weights applied
+to |v|) at most 2e-5 for float32 and 1e-2 for bfloat16 k, v, y.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import scaled_error, wkv_direct, wkv_direct_at, wkv_recurrent
+from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+from rwkv_linear_attention_libwkv_amd.workloads import round_to_bf16
+from tests.gpu_util import TOL, host, run_forward, to_device
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = [("seq", 0), ("chunked", 64), ("chunked", 128), ("chunked", 256)]
+
+
+def check(inp, algos=ALGOS, direct=False):
+    if direct:
+        y_ref, s_ref = wkv_direct(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    else:
+        y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    dev = to_device(inp)
+    for algo, cl in algos:
+        y = host(run_forward(dev, algo, cl))
+        err = scaled_error(y, y_ref, s_ref)
+        print(f"  {algo:8s} chunk {cl:3d}: scaled error {err:.3e}", flush=True)
+        assert err <= TOL[inp["dtype"]], (algo, cl, err)
+
+
+def test_small_workload_all_algorithms():
+    """B=1, T=64, C=64 float32 against the direct O(T^2) sums."""
+    check(workloads.forward_inputs(workloads.FWD_SMALL), direct=True)
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 1, 7), (1, 2, 3), (3, 127, 100), (2, 129, 65),
+                                   (1, 257, 130), (2, 300, 64), (1, 700, 1)])
+def test_ragged_shapes(B, T, C):
+    check(workloads.forward_inputs(workloads.FWD_SMALL.with_(B=B, T=T, C=C, seed=B * 1000 + T + C)))
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_tile_boundaries(chunk):
+    for T in (chunk - 1, chunk, chunk + 1, 3 * chunk + 5):
+        inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=2, T=T, C=70, seed=T))
+        check(inp, algos=[("chunked", chunk), ("seq", 0)])
+
+
+def test_169m_width_workload():
+    """B=8, T=1024, C=768 float32: full tensor against the recurrence, samples against the sums."""
+    spec = workloads.FWD_169M
+    inp = workloads.forward_inputs(spec)
+    check(inp, algos=[("auto", 0), ("seq", 0), ("chunked", 128), ("chunked", 256)])
+    dev = to_device(inp)
+    y = host(run_forward(dev))
+    for (b, c) in workloads.sample_lanes(spec.B, spec.C, 8):
+        for t in (0, 1, 511, spec.T - 1):
+            yt, st = wkv_direct_at(inp["w"][c], inp["u"][c], inp["k"][b, :, c], inp["v"][b, :, c], t)
+            assert abs(y[b, t, c] - yt) <= TOL["f32"] * st
+
+
+def test_bf16_io():
+    """bfloat16 k, v, y with float32 state on a shortened long-context workload."""
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(T=2048, C=512))
+    check(inp, algos=[("seq", 0), ("chunked", 128), ("chunked", 256)])
+
+
+def test_bf16_output_is_rounded_float32_output():
+    """The bf16 path computes in float32 and rounds y to nearest-even once."""
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(T=600, C=192))
+    dev = to_device(inp)
+    dev32 = dict(dev, k=dev["k"].float(), v=dev["v"].float())
+    for algo, cl in (("seq", 0), ("chunked", 128)):
+        y16 = run_forward(dev, algo, cl).view(torch.int16).cpu().numpy()
+        y32 = run_forward(dev32, algo, cl).cpu().numpy()
+        want = round_to_bf16(y32).view(np.uint32) >> 16
+        assert np.array_equal(y16.astype(np.uint16), want.astype(np.uint16)), algo
+
+
+def test_deterministic():
+    inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=3, T=2000, C=200, k_std=2.0))
+    dev = to_device(inp)
+    for algo, cl in (("seq", 0), ("chunked", 64)):
+        a = run_forward(dev, algo, cl)
+        b = run_forward(dev, algo, cl)
+        assert torch.equal(a, b), algo
+
+
+def test_state_handoff_matches_single_pass():
+    """forward(T1) -> state -> forward(T - T1 from state) equals forward(T) (constant-size state)."""
+    inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=2, T=900, C=96, k_std=2.0, seed=3))
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    dev = to_device(inp)
+    for algo, cl in (("seq", 0), ("chunked", 128)):
+        first = dict(dev, k=dev["k"][:, :333].contiguous(), v=dev["v"][:, :333].contiguous())
+        rest = dict(dev, k=dev["k"][:, 333:].contiguous(), v=dev["v"][:, 333:].contiguous())
+        y1, st = run_forward(first, algo, cl, return_state=True)
+        y2 = run_forward(rest, algo, cl, state=st)
+        y = np.concatenate([host(y1), host(y2)], axis=1)
+        assert scaled_error(y, y_ref, s_ref) <= TOL["f32"], algo
+
+
+def test_final_state_matches_oracle():
+    inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=2, T=500, C=80, k_std=2.0, seed=4))
+    _, (a, b, p) = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_state=True)
+    dev = to_device(inp)
+    for algo, cl in (("seq", 0), ("chunked", 64), ("chunked", 256)):
+        _, (ga, gb, gp) = run_forward(dev, algo, cl, return_state=True)
+        ga, gb, gp = host(ga), host(gb), host(gp)
+        np.testing.assert_allclose(gp + np.log(gb), p + np.log(b), rtol=0, atol=2e-5)
+        np.testing.assert_allclose(ga / gb, a / b, rtol=0, atol=2e-5 * np.max(np.abs(inp["v"])))
+
+
+# ---- invariants and special cases on the GPU ----
+
+def special(B=2, T=400, C=70, seed=9, **kw):
+    return workloads.forward_inputs(workloads.FWD_SMALL.with_(B=B, T=T, C=C, seed=seed, **kw))
+
+
+def run_all(inp):
+    dev = to_device(inp)
+    return [(algo, cl, host(run_forward(dev, algo, cl))) for algo, cl in ALGOS]
+
+
+def test_constant_v():
+    inp = special(k_std=2.0)
+    inp["v"][:] = np.float32(-1.25)
+    for algo, cl, y in run_all(inp):
+        np.testing.assert_allclose(y, -1.25, rtol=1e-5, err_msg=f"{algo} {cl}")
+
+
+def test_single_token_gives_v():
+    inp = special(T=1, C=300)
+    for algo, cl, y in run_all(inp):
+        np.testing.assert_allclose(y, inp["v"], rtol=1e-6, atol=0, err_msg=algo)
+
+
+@pytest.mark.parametrize("shift", [200.0, -200.0])
+def test_key_shift(shift):
+    """k + 200 overflows a naive float32 exponential; the result must not change."""
+    inp = special(k_std=2.0)
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    inp["k"] = (inp["k"].astype(np.float64) + shift).astype(np.float32)
+    y_ref2, s_ref2 = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    assert scaled_error(y_ref2, y_ref, s_ref) < 1e-5  # the float32 rounding of k+shift itself
+    for algo, cl, y in run_all(inp):
+        assert scaled_error(y, y_ref2, s_ref2) <= TOL["f32"], (algo, cl)
+
+
+def test_u_equal_w_large_gives_current_v():
+    inp = special()
+    inp["w"][:] = 60.0
+    inp["u"][:] = 60.0
+    for algo, cl, y in run_all(inp):
+        np.testing.assert_allclose(y, inp["v"], rtol=1e-6, atol=1e-30, err_msg=algo)
+
+
+def test_large_w_keeps_newest_past_token():
+    inp = special()
+    inp["w"][:] = 1000.0
+    k = inp["k"].astype(np.float64)
+    v = inp["v"].astype(np.float64)
+    u = inp["u"].astype(np.float64)
+    want = np.empty_like(v)
+    want[:, 0] = v[:, 0]
+    ep, ec = np.exp(k[:, :-1]), np.exp(u[None, None, :] + k[:, 1:])
+    want[:, 1:] = (ep * v[:, :-1] + ec * v[:, 1:]) / (ep + ec)
+    for algo, cl, y in run_all(inp):
+        np.testing.assert_allclose(y, want, rtol=3e-6, atol=3e-6, err_msg=algo)
+
+
+@pytest.mark.parametrize("case", ["negative_w", "huge_k_range", "huge_u", "tiny_u", "w_zero"])
+def test_exact_fallback_cases(case):
+    """Inputs outside the fast path's conditioning run the exact per-token path."""
+    inp = special(T=300, C=130, seed=11)
+    if case == "negative_w":
+        inp["w"][::3] = -0.05
+    elif case == "huge_k_range":
+        inp["k"][:, ::37, ::5] = 90.0
+        inp["k"][:, 5::41, 1::7] = -90.0
+    elif case == "huge_u":
+        inp["u"][::4] = 70.0
+    elif case == "tiny_u":
+        inp["u"][::4] = -70.0
+    elif case == "w_zero":
+        inp["w"][:] = 0.0
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    for algo, cl, y in run_all(inp):
+        assert scaled_error(y, y_ref, s_ref) <= TOL["f32"], (case, algo, cl)
+
+
+def test_nan_propagates():
+    inp = special(T=200, C=64)
+    inp["k"][0, 50, 3] = np.nan
+    inp["v"][1, 120, 7] = np.nan
+    for algo, cl, y in run_all(inp):
+        assert np.all(np.isnan(y[0, 50:, 3])), algo
+        assert np.all(np.isnan(y[1, 120:, 7])), algo
+        assert np.all(np.isfinite(y[0, :50, 3])) and np.all(np.isfinite(y[:, :, 8:])), algo
