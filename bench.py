@@ -93,8 +93,8 @@ def forward_case(spec, steps, warmup, gen="numpy"):
         k = (torch.randn(shape, generator=g, device="cuda") * spec.k_std).to(dt)
         v = (torch.randn(shape, generator=g, device="cuda") * spec.v_std).to(dt)
     y = torch.empty_like(k)
-    need = libwkv.wkv_forward_workspace_bytes(spec.B, spec.T, spec.C, dt)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws = libwkv.new_workspace(spec.B, spec.T, spec.C, dt)
+    need = ws is not None
 
     def fn():
         libwkv.wkv_forward(w, u, k, v, y=y, workspace=ws)

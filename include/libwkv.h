@@ -25,8 +25,10 @@
  *  - Pointers are DEVICE pointers on the current HIP device; the caller owns
  *    every buffer.  Tensors are dense and row-major with the channel index
  *    fastest: k, v, y are [B, T, C] (forward) or [N, G, C] (step).
- *  - Calls are asynchronous on `stream` (0 = the null stream): the library
- *    never synchronises, never allocates and keeps no state between calls.
+ *  - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *    allocate; only wkv_forward_workspace_query synchronises.  The library
+ *    keeps no state of its own: what a chunked forward call carries to the
+ *    next one (a launch counter) lives in the caller's workspace.
  *  - All argument checks happen before any HIP call.  A negative size, or a
  *    NULL pointer for a non-empty operand, gives WKV_EINVAL; an unknown dtype
  *    gives WKV_EDTYPE; a workspace smaller than the query gives
@@ -75,7 +77,7 @@ typedef enum wkv_algo {
 #define WKV_P_EMPTY (-1.0e38f)
 
 /* Chunk lengths (time steps per workgroup tile) accepted by the chunked
- * algorithm; 0 selects the default for the dtype. */
+ * algorithm; 0 selects 256. */
 #define WKV_CHUNK_LENS {64, 128, 256}
 
 /*
@@ -88,6 +90,28 @@ size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt
                                    wkv_algo algo, int64_t chunk_len);
 
 /*
+ * Zero-fill a forward workspace (asynchronously, on `stream`).  Every
+ * workspace must start zero-filled -- through this call or any other fill
+ * with zeros -- before its first use by wkv_forward*; the forward calls keep
+ * it valid afterwards, for any later problem size that fits.  ws_bytes must
+ * be a multiple of 4 and ws 4-byte aligned (WKV_EINVAL otherwise).
+ */
+wkv_status wkv_forward_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Diagnostics of a forward workspace, read after the calls queued on `stream`
+ * have finished (this call synchronises `stream`):
+ *   *gave_up : non-zero if the last chunked call on this workspace stopped
+ *              waiting for a predecessor tile (its bounded spin ran out); the
+ *              outputs of that call are then not valid.  Never expected.
+ *   *epoch   : launch counter of the chunked calls made on this workspace.
+ * WKV_EINVAL for NULL pointers, WKV_EWORKSPACE if ws_bytes cannot hold the
+ * control block, WKV_EHIP if the synchronisation or copy fails.
+ */
+wkv_status wkv_forward_workspace_query(const void* ws, size_t ws_bytes, uint32_t* gave_up,
+                                       uint32_t* epoch, hipStream_t stream);
+
+/*
  * Whole-sequence WKV (the page's time-parallel training mode, section
  * "Transformer-유사학습": every op runs over batch and time at once and only
  * WKV runs as a scan).
@@ -95,9 +119,10 @@ size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt
  *   k, v : [B, T, C] device arrays of dtype dt (read only).
  *   y    : [B, T, C] device array of dtype dt (written).
  *   ws   : device workspace of at least wkv_forward_workspace_bytes(...)
- *          bytes; its contents on entry do not matter and are overwritten.
- *          One workspace must not be used by two calls that may run at the
- *          same time.
+ *          bytes, zero-filled before its first use (wkv_forward_workspace_init)
+ *          and then owned by the library between calls: the chunked scan keeps
+ *          a launch counter and per-tile records there.  One workspace must not
+ *          be used by two calls that may run at the same time.
  * Starts every lane from the empty state.
  */
 wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,

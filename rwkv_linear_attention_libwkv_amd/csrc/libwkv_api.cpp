@@ -1,6 +1,6 @@
 // libwkv C ABI: argument checks, algorithm and tile planning, workspace carve-up and
 // launches on the caller's stream.  Every check runs before any HIP call; nothing here
-// allocates, synchronises or keeps state between calls.
+// allocates or keeps state between calls, and only the workspace query synchronises.
 #include <stddef.h>
 #include <stdint.h>
 
@@ -12,7 +12,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kDefaultTile = 128;
+constexpr int kDefaultTile = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -21,9 +21,13 @@ size_t dtype_size(wkv_dtype dt) { return dt == WKV_F32 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Channels per thread of the forward kernels.  Only one channel per thread is built at
-// present: wider rows push the kernels past four waves per SIMD.
-constexpr int kFwdMaxNch = 1;
+// Channels per thread: the sequential kernel is built for one; the chunked kernel for one
+// or two.  Two channels give 4-byte bf16 rows (2-byte loads run the bf16 tile at a
+// fraction of the float32 rate); float32 rows are 4 bytes already and one channel per
+// thread keeps twice the tiles in flight, which measured faster.
+constexpr int kSeqMaxNch = 1;
+constexpr int kChunkMaxNch = 2;
+int chunk_max_nch(wkv_dtype dt) { return dt == WKV_BF16 ? 2 : 1; }
 
 // Channels per thread: 4, 2 or 1, the largest that divides C and keeps the rows aligned.
 int pick_nch(int64_t C, size_t elt, int max_nch, const void* k, const void* v, const void* y) {
@@ -47,18 +51,34 @@ int resolve_algo(wkv_algo algo, int64_t B, int64_t T, int64_t C) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace bytes of the chunked algorithm for a given channels-per-thread choice.
-size_t chunked_bytes(int64_t B, int64_t T, int64_t C, int tile, int nch) {
+// Workspace of the chunked algorithm: [control words][e^{-w} x C][e^{u} x C]
+// [status word per tile][records: per tile and channel, two states of three tagged
+// 64-bit words].
+struct ChunkLayout {
+    size_t off_d, off_eu, off_status, off_recs, total;
+};
+
+ChunkLayout chunked_layout(int64_t B, int64_t T, int64_t C, int tile, int nch) {
     const int64_t gw = 64 * nch;
     const int64_t n_groups = B * ceil_div(C, gw);
     const int64_t n_tiles = n_groups * ceil_div(T, tile);
-    return kAlign + align_up((size_t)n_tiles * 4, kAlign) + (size_t)n_tiles * 2 * 3 * gw * 4 + kAlign;
+    ChunkLayout L;
+    L.off_d = align_up((size_t)wkv::kCtrlWords * 4, kAlign);
+    L.off_eu = L.off_d + align_up((size_t)C * 4, kAlign);
+    L.off_status = L.off_eu + align_up((size_t)C * 4, kAlign);
+    L.off_recs = L.off_status + align_up((size_t)n_tiles * 4, kAlign);
+    L.total = L.off_recs + (size_t)n_tiles * 2 * 3 * gw * 8 + kAlign;  // + slack to align the base
+    return L;
+}
+
+size_t chunked_bytes(int64_t B, int64_t T, int64_t C, int tile, int nch) {
+    return chunked_layout(B, T, C, tile, nch).total;
 }
 
 // Upper bound over the channels-per-thread choices the launch may make.
 size_t chunked_bytes_bound(int64_t B, int64_t T, int64_t C, int tile) {
     size_t m = 0;
-    for (int n = 1; n <= kFwdMaxNch; n *= 2) {
+    for (int n = 1; n <= kChunkMaxNch; n *= 2) {
         const size_t s = chunked_bytes(B, T, C, tile, n);
         if (s > m) m = s;
     }
@@ -115,24 +135,27 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     const int resolved = resolve_algo(algo, B, T, C);
     if (resolved == WKV_ALGO_SEQ) {
         if (B > 65535) return WKV_EINVAL;  // batch rows are grid.y
-        const int nch = pick_nch(C, elt, kFwdMaxNch, k, v, y);
+        const int nch = pick_nch(C, elt, kSeqMaxNch, k, v, y);
         return wkv::launch_fwd_seq(a, dtype, nch, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
     }
 
     const int tile = chunk_len ? (int)chunk_len : kDefaultTile;
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
-    const int nch = pick_nch(C, elt, kFwdMaxNch, k, v, y);
+    const int nch = pick_nch(C, elt, chunk_max_nch(dt), k, v, y);
     const int64_t gw = 64 * nch;
     a.groups_per_row = (int)ceil_div(C, gw);
     a.n_groups = (int)(B * a.groups_per_row);
     a.n_chunks = (int)ceil_div(T, tile);
     const int64_t n_tiles = (int64_t)a.n_groups * a.n_chunks;
     if (n_tiles > INT_MAX) return WKV_EINVAL;
+    const ChunkLayout L = chunked_layout(B, T, C, tile, nch);
     char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
     a.ctrl = reinterpret_cast<uint32_t*>(base);
-    a.flags = reinterpret_cast<uint32_t*>(base + kAlign);
-    a.recs = reinterpret_cast<float*>(base + kAlign + align_up((size_t)n_tiles * 4, kAlign));
+    a.chan_d = reinterpret_cast<float*>(base + L.off_d);
+    a.chan_eu = reinterpret_cast<float*>(base + L.off_eu);
+    a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
+    a.recs = base + L.off_recs;
     return wkv::launch_fwd_chunked(a, dtype, nch, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
@@ -147,6 +170,26 @@ size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt
     if (B == 0 || T == 0 || C == 0) return 0;
     if (resolve_algo(algo, B, T, C) == WKV_ALGO_SEQ) return 0;
     return chunked_bytes_bound(B, T, C, chunk_len ? (int)chunk_len : kDefaultTile);
+}
+
+wkv_status wkv_forward_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (ws_bytes == 0) return WKV_OK;
+    if (!ws || ws_bytes % 4 != 0 || !aligned(ws, 4)) return WKV_EINVAL;
+    return wkv::launch_zero_words(ws, ws_bytes / 4, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
+wkv_status wkv_forward_workspace_query(const void* ws, size_t ws_bytes, uint32_t* gave_up,
+                                       uint32_t* epoch, hipStream_t stream) {
+    if (!ws || !gave_up || !epoch) return WKV_EINVAL;
+    const uintptr_t base = align_up(reinterpret_cast<uintptr_t>(ws), kAlign);
+    if (ws_bytes < (base - reinterpret_cast<uintptr_t>(ws)) + (size_t)wkv::kCtrlWords * 4)
+        return WKV_EWORKSPACE;
+    const uint32_t* ctrl = reinterpret_cast<const uint32_t*>(base);
+    if (hipStreamSynchronize(stream) != hipSuccess) return WKV_EHIP;
+    if (hipMemcpy(gave_up, ctrl + wkv::kCtrlGiveUp, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(epoch, ctrl + wkv::kCtrlEpoch, 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return WKV_EHIP;
+    return WKV_OK;
 }
 
 wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,

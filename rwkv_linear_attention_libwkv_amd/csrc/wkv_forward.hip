@@ -285,12 +285,11 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         float kk[NCH][L], vv[NCH][L];
         load_chunk<IO, NCH, L>(w, nv, true, kk, vv);
         float R[NCH];
-        bool ok = chan_ok;
+        bool ok = chan_ok && nv == L;  // the ragged last chunk walks exactly
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             float kmax, kmin;
-            if (nv == L) k_range<L, false>(kk[i], nv, kmax, kmin);
-            else k_range<L, true>(kk[i], nv, kmax, kmin);
+            k_range<L, false>(kk[i], L, kmax, kmin);
             st[i] = normalize(st[i]);
             R[i] = kmax * kLog2e;
             const float range = (kmax - kmin) * kLog2e;
@@ -302,10 +301,9 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
             for (int i = 0; i < NCH; ++i) {
 #pragma unroll
                 for (int j = 0; j < L; ++j) kk[i][j] = ex2(fmaf(kk[i][j], kLog2e, -R[i]));
-                if (nv == L) st[i] = fast_outputs<L, false>(ch[i], st[i], R[i], kk[i], vv[i], nv);
-                else st[i] = fast_outputs<L, true>(ch[i], st[i], R[i], kk[i], vv[i], nv);
+                st[i] = fast_outputs<L, false>(ch[i], st[i], R[i], kk[i], vv[i], L);
             }
-            store_chunk<IO, NCH, L>(w, nv, kk);
+            store_chunk<IO, NCH, L>(w, L, kk);
         } else {
             lse_walk<IO, NCH, true>(ch, st, w, nv, true, true);
         }
@@ -326,31 +324,64 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
 // ----------------------------------------------------------------------------
 // Chunked single-pass kernel
 // ----------------------------------------------------------------------------
+//
+// Records.  Every tile publishes, per channel, two states: slot 0 the aggregate of
+// the tile alone, slot 1 the inclusive state after the tile (float32 form, see
+// rec_form).  Each of a, b, p is stored as its own 64-bit word (value | tag << 32)
+// with tag = (epoch << 2) | kind; the epoch is bumped by the prep kernel at every
+// launch, so a word belongs to this launch exactly when its tag matches.  Words are
+// written and read with device-scope atomics (single-copy atomic at 64 bits), so a
+// reader never accepts a torn or stale value and no fence or store-drain is needed.
+// A per-tile status word (the strongest kind published) lets a look-back inspect 64
+// consecutive chunks of a group in one contiguous read; it is only a hint: every
+// record word the fold consumes is re-validated by its own tag.
+//
+// Layout: status[g][chunk] (u32), so one look-back read covers 64 consecutive chunks
+// of its group, and rec[chunk][g][slot][comp][col] (u64, comp = a, b, p).  Records are
+// chunk-major because the tiles in flight at any moment share a chunk index and have
+// consecutive groups: their records then form one dense region instead of landing a
+// large power-of-two stride apart, which would pile the traffic onto a few channels.
 
-// Published per-tile state: record `slot` (0 = aggregate of the tile alone,
-// 1 = inclusive state after the tile) of tile `tix`, laid out [a | b | p] x GW floats.
-template <int GW>
-__device__ __forceinline__ float* tile_record(float* recs, long tix, int slot) {
-    return recs + ((size_t)tix * 2 + slot) * (size_t)(3 * GW);
-}
+constexpr uint32_t kKindAgg = 1u;
+constexpr uint32_t kKindIncl = 2u;
+constexpr uint32_t kMaxSpins = 1u << 18;
+constexpr int kFoldBatch = 4;  // aggregate records loaded per round of the forward fold
+constexpr int kPollSleep = 2;  // s_sleep between polls (units of 64 clocks)
 
-// Coherent (device-scope, cache-bypassing) word stores and loads for the records:
-// they carry sc1 so that another XCD's L2 never serves or holds a stale copy.
-__device__ __forceinline__ void st_dev(float* p, float x) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(x), __ATOMIC_RELAXED,
+struct TileRecs {
+    uint64_t* rec;     // records of chunk 0 of this group
+    uint32_t* status;  // this group's status words
+    int GW;
+    size_t chunk_words;  // words per chunk index over all groups: n_groups * 6 * GW
+    uint32_t tag_agg, tag_incl;
+    __device__ __forceinline__ uint64_t* word(int chunk, int slot, int comp, int col) const {
+        return rec + (size_t)chunk * chunk_words + (size_t)(slot * 3 + comp) * GW + col;
+    }
+};
+
+__device__ __forceinline__ void st_word(uint64_t* p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_dev(const float* p) {
-    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Every earlier vector-memory access of this wave completes before any later one is
-// issued.  With the sc1 accesses above this makes a record visible before its flag.
-__device__ __forceinline__ void vmem_order() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0), other counters untouched
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+// Publish the record of `slot` for this lane's channels, then the tile's status hint.
+template <int NCH>
+__device__ __forceinline__ void publish(const TileRecs& R, int chunk, int slot, int lane,
+                                        const Carry (&c)[NCH], uint32_t tag) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int col = lane * NCH + i;
+        st_word(R.word(chunk, slot, 0, col), c[i].a, tag);
+        st_word(R.word(chunk, slot, 1, col), c[i].b, tag);
+        st_word(R.word(chunk, slot, 2, col), (float)c[i].p, tag);
+    }
+    if (lane == 0)
+        __hip_atomic_store(&R.status[chunk], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The float32 form a state takes in a record: float32 reference pf and the exact
@@ -369,42 +400,51 @@ __device__ __forceinline__ Carry advance(const Carry& prev, const Carry& agg, do
     return rec_form(combine(normalize(prev), agg, decay));
 }
 
-template <int NCH, int GW>
-__device__ __forceinline__ void publish(float* rec, int lane, const Carry (&c)[NCH]) {
+// Raise the give-up flag (once per wave) and report failure.
+__device__ __forceinline__ bool give_up(const FwdArgs& args, int lane) {
+    if (lane == 0) atomicOr(&args.ctrl[kCtrlGiveUp], 1u);
+    return false;
+}
+
+__device__ __forceinline__ bool gave_up_elsewhere(const FwdArgs& args) {
+    return __hip_atomic_load(&args.ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+__device__ __forceinline__ bool should_stop(const FwdArgs& args, uint32_t spin) {
+    return spin >= kMaxSpins || ((spin & 31u) == 31u && gave_up_elsewhere(args));
+}
+
+// Read the record of (chunk, slot) for this lane's channels, re-reading until every
+// word carries `tag`.  Returns false after giving up.
+template <int NCH>
+__device__ __forceinline__ bool read_record(const FwdArgs& args, const TileRecs& R, int chunk, int slot,
+                                            uint32_t tag, int lane, Carry (&out)[NCH]) {
+    for (uint32_t spin = 0;; ++spin) {
+        bool good = true;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int col = lane * NCH + i;  // c[i] is already in record form
-        st_dev(rec + col, c[i].a);
-        st_dev(rec + GW + col, c[i].b);
-        st_dev(rec + 2 * GW + col, (float)c[i].p);
+        for (int i = 0; i < NCH; ++i) {
+            const int col = lane * NCH + i;
+            const uint64_t a = ld_word(R.word(chunk, slot, 0, col));
+            const uint64_t b = ld_word(R.word(chunk, slot, 1, col));
+            const uint64_t p = ld_word(R.word(chunk, slot, 2, col));
+            good = good && word_tag(a) == tag && word_tag(b) == tag && word_tag(p) == tag;
+            out[i] = Carry{word_val(a), word_val(b), (double)word_val(p)};
+        }
+        if (__all(good)) return true;
+        if (should_stop(args, spin)) return give_up(args, lane);
+        __builtin_amdgcn_s_sleep(kPollSleep);
     }
 }
 
-template <int NCH, int GW>
-__device__ __forceinline__ void read_record(const float* rec, int lane, Carry (&c)[NCH]) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int col = lane * NCH + i;
-        c[i].a = ld_dev(rec + col);
-        c[i].b = ld_dev(rec + GW + col);
-        c[i].p = (double)ld_dev(rec + 2 * GW + col);
-    }
-}
-
-constexpr uint32_t kFlagAgg = 1u;
-constexpr uint32_t kFlagIncl = 2u;
-constexpr uint32_t kMaxSpins = 1u << 18;
-constexpr int kFoldBatch = 8;  // aggregate records loaded per round of the forward fold
-
-// Look-back for tile (chunk ci, group g): the state entering the tile.  Lane l polls the
-// tile l+1 chunks back until the nearest inclusive record is found with every record
+// Look-back for tile (chunk ci): the state entering the tile.  Lane l reads the status
+// of the chunk l+1 back until the nearest inclusive record is found with every chunk
 // after it published; the state is then folded forward from that inclusive record
-// through the aggregates in chunk order with advance(), which reproduces the canonical
-// chain bit for bit.  Gives up (raising ctrl[1]) after kMaxSpins polls or as soon as
-// another tile has given up, so every wave always finishes.  Returns false if it gave up.
-template <int NCH, int GW, int TILE>
-__device__ __forceinline__ bool look_back(const FwdArgs& args, const Chan (&ch)[NCH], int ci, int g,
-                                          int lane, Carry (&out)[NCH]) {
+// through the aggregates in chunk order with advance(), reproducing the canonical chain
+// bit for bit.  Gives up (raising the give-up flag) after kMaxSpins polls, or soon after another
+// tile has given up, so every wave always finishes.
+template <int NCH, int TILE>
+__device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan (&ch)[NCH],
+                                          int ci, int lane, Carry (&out)[NCH]) {
     int nearest = ci - 1;  // chunk inspected by lane 0 in the current window
     int start = -1;        // chunk holding the nearest inclusive record
     for (;;) {
@@ -412,12 +452,13 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const Chan (&ch)[
         const int nlanes = min(64, nearest + 1);
         bool window_done = false;
         for (uint32_t spin = 0;; ++spin) {
-            uint32_t st = 0;
-            if (pc >= 0)
-                st = __hip_atomic_load(&args.flags[(long)pc * args.n_groups + g], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t incl = __ballot(pc >= 0 && st == kFlagIncl);
-            const uint64_t ready = __ballot(pc >= 0 && st != 0u);
+            const uint32_t st = pc >= 0 ? __hip_atomic_load(&R.status[pc], __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0u;
+            const bool is_incl = pc >= 0 && st == R.tag_incl;
+            const bool is_ready = is_incl || (pc >= 0 && st == R.tag_agg);
+            const uint64_t incl = __ballot(is_incl);
+            const uint64_t ready = __ballot(is_ready);
             if (incl) {
                 const int d = __builtin_ctzll(incl);
                 const uint64_t need = (d >= 63) ? ~0ull : ((2ull << d) - 1ull);
@@ -426,39 +467,211 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const Chan (&ch)[
                 window_done = true;  // 64 aggregates, no inclusive record yet: look further back
                 break;
             }
-            if (spin >= kMaxSpins ||
-                __hip_atomic_load(&args.ctrl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                if (lane == 0) atomicOr(&args.ctrl[1], 1u);
-                return false;
-            }
-            __builtin_amdgcn_s_sleep(1);
+            if (should_stop(args, spin)) return give_up(args, lane);
+            __builtin_amdgcn_s_sleep(kPollSleep);
         }
         if (!window_done) break;
         nearest -= 64;
     }
-    vmem_order();
+    Carry P[NCH];
+    if (!read_record<NCH>(args, R, start, 1, R.tag_incl, lane, P)) return false;
     double decay[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) decay[i] = (double)TILE * w2_of(ch[i]);
-    Carry P[NCH];
-    read_record<NCH, GW>(tile_record<GW>(args.recs, (long)start * args.n_groups + g, 1), lane, P);
+    // forward fold over the aggregates, kFoldBatch records per round; a round re-reads
+    // its batch until every word's tag matches
 #pragma unroll 1
     for (int c0 = start + 1; c0 < ci; c0 += kFoldBatch) {
-        Carry agg[kFoldBatch][NCH];
+        const int n = min(kFoldBatch, ci - c0);
+        uint64_t t[kFoldBatch][NCH][3];
+        for (uint32_t spin = 0;; ++spin) {
+            bool good = true;
+#pragma unroll
+            for (int j = 0; j < kFoldBatch; ++j)
+                if (j < n)
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) {
+                            t[j][i][q] = ld_word(R.word(c0 + j, 0, q, lane * NCH + i));
+                            good = good && word_tag(t[j][i][q]) == R.tag_agg;
+                        }
+            if (__all(good)) break;
+            if (should_stop(args, spin)) return give_up(args, lane);
+            __builtin_amdgcn_s_sleep(kPollSleep);
+        }
 #pragma unroll
         for (int j = 0; j < kFoldBatch; ++j)
-            if (c0 + j < ci)
-                read_record<NCH, GW>(tile_record<GW>(args.recs, (long)(c0 + j) * args.n_groups + g, 0),
-                                     lane, agg[j]);
+            if (j < n)
 #pragma unroll
-        for (int j = 0; j < kFoldBatch; ++j)
-            if (c0 + j < ci)
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) P[i] = advance(P[i], agg[j][i], decay[i]);
+                for (int i = 0; i < NCH; ++i)
+                    P[i] = advance(P[i],
+                                   Carry{word_val(t[j][i][0]), word_val(t[j][i][1]),
+                                         (double)word_val(t[j][i][2])},
+                                   decay[i]);
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) out[i] = P[i];
     return true;
+}
+
+// Everything a tile's waves share.
+template <int NCH, int L, int NW>
+struct TileShared {
+    int ticket;
+    float a[NW][64 * NCH];  // per-wave aggregate, then the state before each wave
+    float b[NW][64 * NCH];
+    double p[NW][64 * NCH];
+    float ca[64 * NCH];  // state entering the tile
+    float cb[64 * NCH];
+    double cp[64 * NCH];
+    float stash[2 * NCH * L][64];  // wave 0's chunk while it runs the look-back
+};
+
+// The tile after its k, v rows are loaded.  FAST: the wave's chunk is full and well
+// conditioned and stays in registers; otherwise the wave walks its rows in memory with
+// the exact log-sum-exp recurrence.  Both instantiations pass the same two barriers.
+template <typename IO, int NCH, int L, int NW, bool FAST>
+__device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NCH, L, NW>& sh,
+                                          const TileRecs& recs, const WaveRows& rows,
+                                          float (&kk)[NCH][L], float (&vv)[NCH][L],
+                                          const Chan (&ch)[NCH], const float (&R)[NCH], int lane,
+                                          int wid, int g, int ci, int bi, int c, bool cvalid, int nv,
+                                          int t_tile, int tile_len) {
+    constexpr int TILE = L * NW;
+    const int C = args.C, T = args.T;
+
+    // ---- per-wave aggregate of its tokens, from the empty state ----
+    Carry agg[NCH];
+    if constexpr (FAST) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                const float x = ex2(fmaf(kk[i][j], kLog2e, -R[i]));
+                kk[i][j] = x;  // k is replaced by its weight relative to R
+                a = fmaf(ch[i].d, a, x * vv[i][j]);
+                b = fmaf(ch[i].d, b, x);
+            }
+            agg[i] = Carry{a, b, (double)R[i]};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) agg[i] = empty_carry();
+        lse_walk<IO, NCH, false>(ch, agg, rows, nv, cvalid, false);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        sh.a[wid][lane * NCH + i] = agg[i].a;
+        sh.b[wid][lane * NCH + i] = agg[i].b;
+        sh.p[wid][lane * NCH + i] = agg[i].p;
+    }
+    __syncthreads();
+
+    // ---- wave 0: tile aggregate, look-back, publish ----
+    if (wid == 0) {
+        if constexpr (FAST) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+#pragma unroll
+                for (int j = 0; j < L; ++j) {
+                    sh.stash[i * L + j][lane] = kk[i][j];
+                    sh.stash[(NCH + i) * L + j][lane] = vv[i][j];
+                }
+            // the chunk must really leave the registers: no forwarding of the stash
+            asm volatile("" ::: "memory");
+        }
+        Carry run[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) run[i] = empty_carry();
+#pragma unroll 1
+        for (int wv = 0; wv < NW; ++wv) {
+            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int col = lane * NCH + i;
+                const Carry aw{sh.a[wv][col], sh.b[wv][col], sh.p[wv][col]};
+                sh.a[wv][col] = run[i].a;  // slot wv now holds the state before wave wv
+                sh.b[wv][col] = run[i].b;
+                sh.p[wv][col] = run[i].p;
+                run[i] = combine(run[i], aw, (double)nvw * w2_of(ch[i]));
+            }
+        }
+        Carry agg_rec[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) agg_rec[i] = rec_form(run[i]);
+        Carry prefix[NCH];
+        if (ci == 0) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const size_t si = (size_t)bi * C + c + i;
+                prefix[i] = rec_form((args.sin_a && cvalid)
+                                         ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
+                                         : empty_carry());
+            }
+        } else {
+            publish<NCH>(recs, ci, 0, lane, agg_rec, recs.tag_agg);
+            if (!look_back<NCH, TILE>(args, recs, ch, ci, lane, prefix)) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) prefix[i] = empty_carry();
+            }
+        }
+        Carry incl[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+            incl[i] = advance(prefix[i], agg_rec[i], (double)tile_len * w2_of(ch[i]));
+        if (ci + 1 < args.n_chunks) {
+            publish<NCH>(recs, ci, 1, lane, incl, recs.tag_incl);
+        } else if (args.sout_a && cvalid) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const size_t si = (size_t)bi * C + c + i;
+                float a, b, p;
+                carry_to_abi(incl[i], a, b, p);
+                args.sout_a[si] = a;
+                args.sout_b[si] = b;
+                args.sout_p[si] = p;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            sh.ca[lane * NCH + i] = prefix[i].a;
+            sh.cb[lane * NCH + i] = prefix[i].b;
+            sh.cp[lane * NCH + i] = prefix[i].p;
+        }
+        if constexpr (FAST) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+#pragma unroll
+                for (int j = 0; j < L; ++j) {
+                    kk[i][j] = sh.stash[i * L + j][lane];
+                    vv[i][j] = sh.stash[(NCH + i) * L + j][lane];
+                }
+        }
+    }
+    __syncthreads();
+    if (nv == 0) return;
+
+    // ---- outputs of this wave from the state entering its tokens ----
+    Carry cin[NCH];
+    bool out_ok = FAST;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int col = lane * NCH + i;
+        const Carry tile_in{sh.ca[col], sh.cb[col], sh.cp[col]};
+        const Carry before{sh.a[wid][col], sh.b[wid][col], sh.p[wid][col]};
+        cin[i] = normalize(combine(tile_in, before, (double)(wid * L) * w2_of(ch[i])));
+        out_ok = out_ok && (cin[i].p - (double)R[i] <= (double)kSpan);
+    }
+    if (FAST && __all(out_ok)) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) fast_outputs<L, false>(ch[i], cin[i], R[i], kk[i], vv[i], L);
+        if (cvalid) store_chunk<IO, NCH, L>(rows, L, kk);
+    } else {
+        lse_walk<IO, NCH, true>(ch, cin, rows, nv, cvalid, cvalid);
+    }
 }
 
 template <typename IO, int NCH, int L, int NW>
@@ -466,23 +679,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     constexpr int GW = 64 * NCH;
     constexpr int TILE = L * NW;
     const int lane = threadIdx.x & 63;
-    const int wid = threadIdx.x >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
     const int C = args.C, T = args.T;
-
-    __shared__ int s_ticket;
-    __shared__ float s_a[NW][GW];
-    __shared__ float s_b[NW][GW];
-    __shared__ double s_p[NW][GW];
-    __shared__ float s_ca[GW];
-    __shared__ float s_cb[GW];
-    __shared__ double s_cp[GW];
-    __shared__ float s_stash[2 * NCH * L][64];  // wave 0's chunk while it runs the look-back
+    __shared__ TileShared<NCH, L, NW> sh;
 
     // Tiles are numbered in the order workgroups start, so every tile this one waits on
     // has already started and publishes its aggregate without waiting for anything.
-    if (threadIdx.x == 0) s_ticket = (int)atomicAdd(args.ctrl, 1u);
+    if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
     const int g = ticket % args.n_groups;
     const int ci = ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
@@ -503,177 +709,65 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
         rows.lane_off = (uint32_t)(lane * NCH * sizeof(IO));
         rows.row_bytes = (uint32_t)(C * sizeof(IO));
     }
+    TileRecs recs;
+    recs.rec = static_cast<uint64_t*>(args.recs) + (size_t)g * 6 * GW;
+    recs.chunk_words = (size_t)args.n_groups * 6 * GW;
+    recs.status = args.status + (size_t)g * args.n_chunks;
+    recs.GW = GW;
+    recs.tag_agg = (epoch << 2) | kKindAgg;
+    recs.tag_incl = (epoch << 2) | kKindIncl;
 
     float kk[NCH][L], vv[NCH][L];
     load_chunk<IO, NCH, L>(rows, nv, cvalid, kk, vv);
 
     Chan ch[NCH];
-    bool chan_ok = true;
+    bool ok = true;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-        ch[i] = cvalid ? make_chan(args.w[c + i], args.u[c + i]) : make_chan(0.f, 0.f);
-        chan_ok = chan_ok && chan_fast_ok(ch[i]);
+        const int ci_ = cvalid ? c + i : 0;
+        ch[i] = Chan{args.chan_d[ci_], args.chan_eu[ci_], args.w[ci_], args.u[ci_]};
+        ok = ok && chan_fast_ok(ch[i]);
     }
-
-    // ---- per-wave aggregate of its tokens, from the empty state ----
     float R[NCH];
-    bool ok = chan_ok;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         float kmax, kmin;
-        if (nv == L) k_range<L, false>(kk[i], nv, kmax, kmin);
-        else k_range<L, true>(kk[i], nv, kmax, kmin);
+        k_range<L, false>(kk[i], L, kmax, kmin);
         R[i] = kmax * kLog2e;
         const float range = (kmax - kmin) * kLog2e;
         ok = ok && (range <= kSpan) && (range - ch[i].u * kLog2e <= kSpan);
     }
-    const bool fast = __all(ok) && nv > 0;
-    Carry agg[NCH];
-    if (fast) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            float a = 0.f, b = 0.f;
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                const float x = ex2(fmaf(kk[i][j], kLog2e, -R[i]));
-                kk[i][j] = x;  // k is replaced by its weight relative to R
-                if (j < nv) {
-                    a = fmaf(ch[i].d, a, x * vv[i][j]);
-                    b = fmaf(ch[i].d, b, x);
-                }
-            }
-            agg[i] = Carry{a, b, (double)R[i]};
-        }
-    } else {
-        // the register chunk is not used again on this path (outputs walk memory too)
-        drop_chunk<NCH, L>(kk, vv);
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) agg[i] = empty_carry();
-        lse_walk<IO, NCH, false>(ch, agg, rows, nv, cvalid, false);
-    }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        s_a[wid][lane * NCH + i] = agg[i].a;
-        s_b[wid][lane * NCH + i] = agg[i].b;
-        s_p[wid][lane * NCH + i] = agg[i].p;
-    }
-    __syncthreads();
+    // the fast path takes full chunks only; the one ragged chunk at the end of a
+    // sequence (and any ill-conditioned chunk) walks its rows exactly
+    if (__all(ok) && nv == L)
+        tile_body<IO, NCH, L, NW, true>(args, sh, recs, rows, kk, vv, ch, R, lane, wid, g, ci, bi, c,
+                                        cvalid, nv, t_tile, tile_len);
+    else
+        tile_body<IO, NCH, L, NW, false>(args, sh, recs, rows, kk, vv, ch, R, lane, wid, g, ci, bi, c,
+                                         cvalid, nv, t_tile, tile_len);
+}
 
-    // ---- wave 0: tile aggregate, look-back, publish (its chunk waits in LDS) ----
-    if (wid == 0) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                s_stash[i * L + j][lane] = kk[i][j];
-                s_stash[(NCH + i) * L + j][lane] = vv[i][j];
-            }
-        Carry run[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) run[i] = empty_carry();
-#pragma unroll 1
-        for (int wv = 0; wv < NW; ++wv) {
-            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int col = lane * NCH + i;
-                const Carry aw{s_a[wv][col], s_b[wv][col], s_p[wv][col]};
-                s_a[wv][col] = run[i].a;  // slot wv now holds the state before wave wv
-                s_b[wv][col] = run[i].b;
-                s_p[wv][col] = run[i].p;
-                run[i] = combine(run[i], aw, (double)nvw * w2_of(ch[i]));
-            }
-        }
-        const long tix = (long)ci * args.n_groups + g;
-        Carry agg_rec[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) agg_rec[i] = rec_form(run[i]);
-        Carry prefix[NCH];
-        if (ci == 0) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const size_t si = (size_t)bi * C + c + i;
-                prefix[i] = rec_form((args.sin_a && cvalid)
-                                         ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
-                                         : empty_carry());
-            }
-        } else {
-            publish<NCH, GW>(tile_record<GW>(args.recs, tix, 0), lane, agg_rec);
-            vmem_order();
-            if (lane == 0)
-                __hip_atomic_store(&args.flags[tix], kFlagAgg, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (!look_back<NCH, GW, TILE>(args, ch, ci, g, lane, prefix)) {
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) prefix[i] = empty_carry();
-            }
-        }
-        Carry incl[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-            incl[i] = advance(prefix[i], agg_rec[i], (double)tile_len * w2_of(ch[i]));
-        if (ci + 1 < args.n_chunks) {
-            publish<NCH, GW>(tile_record<GW>(args.recs, tix, 1), lane, incl);
-            vmem_order();
-            if (lane == 0)
-                __hip_atomic_store(&args.flags[tix], kFlagIncl, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        } else if (args.sout_a && cvalid) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const size_t si = (size_t)bi * C + c + i;
-                float a, b, p;
-                carry_to_abi(incl[i], a, b, p);
-                args.sout_a[si] = a;
-                args.sout_b[si] = b;
-                args.sout_p[si] = p;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            s_ca[lane * NCH + i] = prefix[i].a;
-            s_cb[lane * NCH + i] = prefix[i].b;
-            s_cp[lane * NCH + i] = prefix[i].p;
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                kk[i][j] = s_stash[i * L + j][lane];
-                vv[i][j] = s_stash[(NCH + i) * L + j][lane];
-            }
+// Per launch: reset the ticket counter and give-up flag, open a new record epoch, and
+// compute the per-channel constants e^{-w} and e^{u} once (float64 exp, rounded).
+__global__ void prep_kernel(uint32_t* __restrict__ ctrl, const float* __restrict__ w,
+                            const float* __restrict__ u, float* __restrict__ cd,
+                            float* __restrict__ ceu, int C) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) {
+        ctrl[kCtrlTicket] = 0u;
+        ctrl[kCtrlGiveUp] = 0u;
+        ctrl[kCtrlEpoch] = (ctrl[kCtrlEpoch] + 1u) & 0x3fffffffu;
     }
-    __syncthreads();
-    if (nv == 0) return;
-
-    // ---- outputs of this wave from the state entering its tokens ----
-    Carry cin[NCH];
-    bool out_ok = fast;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int col = lane * NCH + i;
-        const Carry tile_in{s_ca[col], s_cb[col], s_cp[col]};
-        const Carry before{s_a[wid][col], s_b[wid][col], s_p[wid][col]};
-        cin[i] = normalize(combine(tile_in, before, (double)(wid * L) * w2_of(ch[i])));
-        out_ok = out_ok && (cin[i].p - (double)R[i] <= (double)kSpan);
-    }
-    if (__all(out_ok)) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            if (nv == L) fast_outputs<L, false>(ch[i], cin[i], R[i], kk[i], vv[i], nv);
-            else fast_outputs<L, true>(ch[i], cin[i], R[i], kk[i], vv[i], nv);
-        }
-        if (cvalid) store_chunk<IO, NCH, L>(rows, nv, kk);
-    } else {
-        lse_walk<IO, NCH, true>(ch, cin, rows, nv, cvalid, cvalid);
+    if (i < C) {
+        cd[i] = (float)exp(-(double)w[i]);
+        ceu[i] = (float)exp((double)u[i]);
     }
 }
 
-// Zero the ticket counter, the error word and the per-tile flags before a chunked launch.
-__global__ void clear_words_kernel(uint32_t* __restrict__ ctrl, uint32_t* __restrict__ flags, long n) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < 2) ctrl[i] = 0u;
-    for (long j = i; j < n; j += (long)gridDim.x * blockDim.x) flags[j] = 0u;
+// Zero a workspace (the state every workspace must start from).
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 // State copy used when T = 0 and the caller asked for the state through.
@@ -716,26 +810,37 @@ template <typename IO, int NCH, int NW>
 static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
     constexpr int L = chunk_tokens<NCH>();
     const long n_tiles = (long)a.n_groups * a.n_chunks;
-    const long clear_blocks = std::min<long>(1024, (n_tiles + 255) / 256 + 1);
-    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)clear_blocks), dim3(256), 0, s, a.ctrl,
-                       a.flags, n_tiles);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((a.C + 255) / 256)), dim3(256), 0, s, a.ctrl, a.w,
+                       a.u, a.chan_d, a.chan_eu, a.C);
     hipLaunchKernelGGL((fwd_chunked_kernel<IO, NCH, L, NW>), dim3((unsigned)n_tiles), dim3(64 * NW),
                        0, s, a);
     return hipGetLastError();
 }
 
-// Tile = NW waves x 32 tokens (NCH = 1).
+// Tile = NW waves x (32 / NCH) tokens.
 template <typename IO>
-static hipError_t launch_chunked_n(const FwdArgs& a, int tile, hipStream_t s) {
-    if (tile == 64) return launch_chunked_t<IO, 1, 2>(a, s);
-    if (tile == 128) return launch_chunked_t<IO, 1, 4>(a, s);
-    if (tile == 256) return launch_chunked_t<IO, 1, 8>(a, s);
+static hipError_t launch_chunked_n(const FwdArgs& a, int nch, int tile, hipStream_t s) {
+    if (nch == 2) {
+        if (tile == 64) return launch_chunked_t<IO, 2, 4>(a, s);
+        if (tile == 128) return launch_chunked_t<IO, 2, 8>(a, s);
+        if (tile == 256) return launch_chunked_t<IO, 2, 16>(a, s);
+    } else if (nch == 1) {
+        if (tile == 64) return launch_chunked_t<IO, 1, 2>(a, s);
+        if (tile == 128) return launch_chunked_t<IO, 1, 4>(a, s);
+        if (tile == 256) return launch_chunked_t<IO, 1, 8>(a, s);
+    }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_chunked(const FwdArgs& a, int dtype, int nch, int tile, hipStream_t s) {
-    if (nch != 1) return hipErrorInvalidValue;
-    return dtype == 0 ? launch_chunked_n<float>(a, tile, s) : launch_chunked_n<uint16_t>(a, tile, s);
+    return dtype == 0 ? launch_chunked_n<float>(a, nch, tile, s) : launch_chunked_n<uint16_t>(a, nch, tile, s);
+}
+
+hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s) {
+    const size_t blocks = std::min<size_t>(4096, (n_words + 255) / 256 + 1);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<uint32_t*>(p), n_words);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,

@@ -23,6 +23,8 @@ P_EMPTY = -1.0e38
 #: every function include/libwkv.h declares
 EXPORTS = (
     "wkv_forward_workspace_bytes",
+    "wkv_forward_workspace_init",
+    "wkv_forward_workspace_query",
     "wkv_forward",
     "wkv_forward_ex",
     "wkv_forward_state",
@@ -49,6 +51,11 @@ def _load() -> ctypes.CDLL:
     i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.wkv_forward_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i64]
     lib.wkv_forward_workspace_bytes.restype = sz
+    lib.wkv_forward_workspace_init.argtypes = [vp, sz, vp]
+    lib.wkv_forward_workspace_init.restype = i32
+    lib.wkv_forward_workspace_query.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_uint32),
+                                                ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.wkv_forward_workspace_query.restype = i32
     lib.wkv_forward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wkv_forward.restype = i32
     lib.wkv_forward_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, i32, i64, vp]
@@ -108,6 +115,23 @@ def wkv_forward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32, alg
     return int(n)
 
 
+def wkv_forward_workspace_init(workspace, stream=None):
+    """Zero-fill a forward workspace (needed once, before its first use)."""
+    _check(lib.wkv_forward_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)), "wkv_forward_workspace_init")
+    return workspace
+
+
+def new_workspace(B: int, T: int, C: int, dtype=torch.float32, algo: str = "auto", chunk_len: int = 0,
+                  device="cuda"):
+    """A ready (zero-filled) workspace for these sizes, or None if none is needed."""
+    need = wkv_forward_workspace_bytes(B, T, C, dtype, algo, chunk_len)
+    if not need:
+        return None
+    ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
+    return wkv_forward_workspace_init(ws)
+
+
 def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, workspace=None,
                 state=None, return_state: bool = False, state_out=None, stream=None):
     """y = WKV(w, u, k, v) for k, v of shape [B, T, C] (float32 or bfloat16, on the GPU).
@@ -132,7 +156,7 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
     _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
     need = wkv_forward_workspace_bytes(B, T, C, k.dtype, algo, chunk_len)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+        workspace = new_workspace(B, T, C, k.dtype, algo, chunk_len, device=k.device)
     if workspace is not None:
         _need(workspace.is_cuda and workspace.is_contiguous(), "bad workspace")
     ws_ptr = _ptr(workspace)
@@ -191,14 +215,23 @@ def empty_state(shape, device="cuda"):
     return a, b, p
 
 
-def lookback_error(workspace) -> int:
-    """Non-zero if a chunked call that used ``workspace`` gave up waiting in its look-back.
+def workspace_query(workspace, stream=None):
+    """(gave_up, epoch) of a forward workspace; synchronises the stream first."""
+    g, e = ctypes.c_uint32(0), ctypes.c_uint32(0)
+    _check(lib.wkv_forward_workspace_query(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           ctypes.byref(g), ctypes.byref(e), _stream(stream)),
+           "wkv_forward_workspace_query")
+    return int(g.value), int(e.value)
 
-    Reads the second control word of the workspace (after the call has finished).
-    """
-    base = workspace.data_ptr()
-    off = (-base) % 256
-    return int(workspace[off + 4: off + 8].view(torch.int32).item())
+
+def lookback_error(workspace, stream=None) -> int:
+    """Non-zero if the last chunked call on ``workspace`` gave up waiting in its look-back."""
+    return workspace_query(workspace, stream)[0]
+
+
+def workspace_epoch(workspace, stream=None) -> int:
+    """Launch counter kept in a chunked workspace."""
+    return workspace_query(workspace, stream)[1]
 
 
 # short aliases

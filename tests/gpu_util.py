@@ -22,8 +22,7 @@ def run_forward(dev, algo="auto", chunk_len=0, state=None, return_state=False):
     """Run wkv_forward on device tensors; asserts the look-back never gave up."""
     k = dev["k"]
     B, T, C = k.shape
-    need = libwkv.wkv_forward_workspace_bytes(B, T, C, k.dtype, algo, chunk_len)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device) if need else None
+    ws = libwkv.new_workspace(B, T, C, k.dtype, algo, chunk_len, device=k.device)
     out = libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo=algo, chunk_len=chunk_len,
                              workspace=ws, state=state, return_state=return_state)
     torch.cuda.synchronize()

@@ -96,6 +96,17 @@ def test_workspace_query():
     assert q(1, 64, 64, F32, 0, 0) == 0
 
 
+def test_workspace_diagnostics_argument_checks():
+    g, e = ctypes.c_uint32(), ctypes.c_uint32()
+    wq = lib.wkv_forward_workspace_query
+    assert wq(NULL, 4096, ctypes.byref(g), ctypes.byref(e), None) == EINVAL
+    assert wq(P, 4096, None, ctypes.byref(e), None) == EINVAL
+    assert wq(P, 4096, ctypes.byref(g), None, None) == EINVAL
+    # too small for the control block: rejected before any HIP call
+    assert wq(P, 255, ctypes.byref(g), ctypes.byref(e), None) == EWS
+    assert wq(ctypes.c_void_p(0x1004), 256, ctypes.byref(g), ctypes.byref(e), None) == EWS
+
+
 def test_step_argument_checks():
     def step(N, G, C, dt=BF16, ptrs=(P,) * 8):
         return lib.wkv_step(N, G, C, dt, *ptrs, None)

@@ -68,15 +68,29 @@ def test_bf16_io():
 
 
 def test_bf16_output_is_rounded_float32_output():
-    """The bf16 path computes in float32 and rounds y to nearest-even once."""
+    """The bf16 path computes in float32 and rounds y to nearest-even once.
+
+    The sequential walk does the same float32 operations for both dtypes, so its bf16
+    output is bit for bit the rounded float32 output.  The chunked scan runs two
+    channels per thread for bf16 (one for float32), which changes how many tokens a
+    wave aggregates and so the float32 rounding: there each bf16 output must be the
+    rounding of some float32 value within 1e-6 * s of the float32 path's output
+    (s = the convex weights applied to |v|, the scale of the error metric)."""
     inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(T=600, C=192))
+    _, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
     dev = to_device(inp)
     dev32 = dict(dev, k=dev["k"].float(), v=dev["v"].float())
     for algo, cl in (("seq", 0), ("chunked", 128)):
-        y16 = run_forward(dev, algo, cl).view(torch.int16).cpu().numpy()
+        y16 = run_forward(dev, algo, cl).float().cpu().numpy()
         y32 = run_forward(dev32, algo, cl).cpu().numpy()
-        want = round_to_bf16(y32).view(np.uint32) >> 16
-        assert np.array_equal(y16.astype(np.uint16), want.astype(np.uint16)), algo
+        if algo == "seq":
+            assert np.array_equal(y16, round_to_bf16(y32)), algo
+        else:
+            d = 1e-6 * s_ref
+            lo = round_to_bf16((y32 - d).astype(np.float32))
+            hi = round_to_bf16((y32 + d).astype(np.float32))
+            assert np.all((lo <= y16) & (y16 <= hi)), algo
+            assert np.mean(y16 == round_to_bf16(y32)) >= 0.99, algo
 
 
 def test_deterministic():
@@ -199,3 +213,42 @@ def test_nan_propagates():
         assert np.all(np.isnan(y[0, 50:, 3])), algo
         assert np.all(np.isnan(y[1, 120:, 7])), algo
         assert np.all(np.isfinite(y[0, :50, 3])) and np.all(np.isfinite(y[:, :, 8:])), algo
+
+
+@pytest.mark.parametrize("C", [192, 130])
+def test_long_sequences_every_tile(C):
+    """Hundreds of chunks per channel group: the look-back folds long runs of published
+    aggregates.  Repeated launches on one workspace must agree bit for bit and with the
+    oracle on every element."""
+    inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=2, T=20000, C=C, k_std=1.5, seed=C))
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    dev = to_device(inp)
+    k = dev["k"]
+    for cl in (64, 128, 256):
+        ws = libwkv.new_workspace(2, 20000, C, k.dtype, "chunked", cl)
+        first = None
+        for rep in range(3):
+            y = libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="chunked", chunk_len=cl,
+                                   workspace=ws)
+            torch.cuda.synchronize()
+            assert libwkv.lookback_error(ws) == 0
+            err = scaled_error(host(y), y_ref, s_ref)
+            assert err <= TOL["f32"], (cl, rep, err)
+            if first is None:
+                first = y.clone()
+            else:
+                assert torch.equal(first, y), (cl, rep)
+
+
+def test_workspace_epoch_counts_chunked_calls():
+    """Each chunked call opens a new record epoch; a sequential call leaves it alone."""
+    inp = special(B=1, T=700, C=64)
+    dev = to_device(inp)
+    k = dev["k"]
+    ws = libwkv.new_workspace(1, 700, 64, k.dtype, "chunked", 128)
+    assert libwkv.workspace_query(ws) == (0, 0)
+    for n in range(1, 4):
+        libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="chunked", chunk_len=128, workspace=ws)
+        assert libwkv.workspace_query(ws) == (0, n)
+    libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="seq", workspace=ws)
+    assert libwkv.workspace_query(ws) == (0, 3)
