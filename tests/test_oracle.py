@@ -69,6 +69,9 @@ def test_hand_examples(ex):
     want = np.array([float(Fraction(x)) for x in ex["y"]])
     for y in (wkv_direct(w, u, k, v), wkv_recurrent(w, u, k, v)):
         np.testing.assert_allclose(y[1, :, 1], want, rtol=1e-14, atol=1e-15)
+    # the 50-digit evaluation that pins the float64 forms is itself pinned here
+    y_mp = wkv_mp(w[1:2], u[1:2], k[1:2, :, 1:2], v[1:2, :, 1:2]).astype(np.float64)
+    np.testing.assert_allclose(y_mp[0, :, 0], want, rtol=1e-15, atol=1e-16)
     for t in range(T):
         yt, _ = wkv_direct_at(w[1], u[1], k[1, :, 1], v[1, :, 1], t)
         assert abs(yt - want[t]) <= 1e-14 * max(1.0, abs(want[t]))
