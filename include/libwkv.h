@@ -78,7 +78,7 @@ typedef enum wkv_algo {
 
 /* Chunk lengths (time steps per workgroup tile) accepted by the chunked
  * algorithm; 0 selects 256. */
-#define WKV_CHUNK_LENS {64, 128, 256}
+#define WKV_CHUNK_LENS {64, 128, 256, 512}
 
 /*
  * Bytes of device workspace that wkv_forward_ex needs for this problem with

@@ -21,24 +21,15 @@ size_t dtype_size(wkv_dtype dt) { return dt == WKV_F32 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Channels per thread: the sequential kernel is built for one; the chunked kernel for one
-// or two.  Two channels give 4-byte bf16 rows (2-byte loads run the bf16 tile at a
-// fraction of the float32 rate); float32 rows are 4 bytes already and one channel per
-// thread keeps twice the tiles in flight, which measured faster.
-constexpr int kSeqMaxNch = 1;
-constexpr int kChunkMaxNch = 2;
-int chunk_max_nch(wkv_dtype dt) { return dt == WKV_BF16 ? 2 : 1; }
-
-// Channels per thread: 4, 2 or 1, the largest that divides C and keeps the rows aligned.
-int pick_nch(int64_t C, size_t elt, int max_nch, const void* k, const void* v, const void* y) {
-    for (int n = max_nch; n > 1; n /= 2) {
-        const size_t bytes = elt * (size_t)n;
-        if (C % n == 0 && aligned(k, bytes) && aligned(v, bytes) && aligned(y, bytes)) return n;
-    }
-    return 1;
+// The chunked kernel moves bfloat16 rows two at a time (4 bytes per lane) when C is even
+// and k, v, y are 4-byte aligned; 2-byte lanes otherwise.
+int chunk_io(wkv_dtype dt, int64_t C, const void* k, const void* v, const void* y) {
+    if (dt == WKV_F32) return wkv::kIoF32;
+    const bool pairs = C % 2 == 0 && aligned(k, 4) && aligned(v, 4) && aligned(y, 4);
+    return pairs ? wkv::kIoBf16Pair : wkv::kIoBf16;
 }
 
-bool tile_ok(int64_t t) { return t == 0 || t == 64 || t == 128 || t == 256; }
+bool tile_ok(int64_t t) { return t == 0 || t == 64 || t == 128 || t == 256 || t == 512; }
 
 // AUTO: enough (b, c) lanes to fill the chip, or a sequence shorter than one tile, walks
 // T sequentially; otherwise T is split into tiles.
@@ -51,38 +42,24 @@ int resolve_algo(wkv_algo algo, int64_t B, int64_t T, int64_t C) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace of the chunked algorithm: [control words][e^{-w} x C][e^{u} x C]
-// [status word per tile][records: per tile and channel, two states of three tagged
-// 64-bit words].
+// Workspace of the chunked algorithm: [control words][status word per tile][records: per
+// tile and channel, two states of three tagged 64-bit words].
 struct ChunkLayout {
-    size_t off_d, off_eu, off_status, off_recs, total;
+    size_t off_status, off_recs, total;
 };
 
-ChunkLayout chunked_layout(int64_t B, int64_t T, int64_t C, int tile, int nch) {
-    const int64_t gw = 64 * nch;
-    const int64_t n_groups = B * ceil_div(C, gw);
+ChunkLayout chunked_layout(int64_t B, int64_t T, int64_t C, int tile) {
+    const int64_t n_groups = B * ceil_div(C, 64);
     const int64_t n_tiles = n_groups * ceil_div(T, tile);
     ChunkLayout L;
-    L.off_d = align_up((size_t)wkv::kCtrlWords * 4, kAlign);
-    L.off_eu = L.off_d + align_up((size_t)C * 4, kAlign);
-    L.off_status = L.off_eu + align_up((size_t)C * 4, kAlign);
+    L.off_status = align_up((size_t)wkv::kCtrlWords * 4, kAlign);
     L.off_recs = L.off_status + align_up((size_t)n_tiles * 4, kAlign);
-    L.total = L.off_recs + (size_t)n_tiles * 2 * 3 * gw * 8 + kAlign;  // + slack to align the base
+    L.total = L.off_recs + (size_t)n_tiles * 2 * 3 * 64 * 8 + kAlign;  // + slack to align the base
     return L;
 }
 
-size_t chunked_bytes(int64_t B, int64_t T, int64_t C, int tile, int nch) {
-    return chunked_layout(B, T, C, tile, nch).total;
-}
-
-// Upper bound over the channels-per-thread choices the launch may make.
 size_t chunked_bytes_bound(int64_t B, int64_t T, int64_t C, int tile) {
-    size_t m = 0;
-    for (int n = 1; n <= kChunkMaxNch; n *= 2) {
-        const size_t s = chunked_bytes(B, T, C, tile, n);
-        if (s > m) m = s;
-    }
-    return m;
+    return chunked_layout(B, T, C, tile).total;
 }
 
 bool sizes_ok(int64_t B, int64_t T, int64_t C) {
@@ -131,32 +108,27 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.C = (int)C;
 
     const int dtype = dt == WKV_F32 ? 0 : 1;
-    const size_t elt = dtype_size(dt);
     const int resolved = resolve_algo(algo, B, T, C);
     if (resolved == WKV_ALGO_SEQ) {
         if (B > 65535) return WKV_EINVAL;  // batch rows are grid.y
-        const int nch = pick_nch(C, elt, kSeqMaxNch, k, v, y);
-        return wkv::launch_fwd_seq(a, dtype, nch, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+        return wkv::launch_fwd_seq(a, dtype, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
     }
 
     const int tile = chunk_len ? (int)chunk_len : kDefaultTile;
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
-    const int nch = pick_nch(C, elt, chunk_max_nch(dt), k, v, y);
-    const int64_t gw = 64 * nch;
-    a.groups_per_row = (int)ceil_div(C, gw);
+    a.groups_per_row = (int)ceil_div(C, 64);
     a.n_groups = (int)(B * a.groups_per_row);
     a.n_chunks = (int)ceil_div(T, tile);
     const int64_t n_tiles = (int64_t)a.n_groups * a.n_chunks;
     if (n_tiles > INT_MAX) return WKV_EINVAL;
-    const ChunkLayout L = chunked_layout(B, T, C, tile, nch);
+    const ChunkLayout L = chunked_layout(B, T, C, tile);
     char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
     a.ctrl = reinterpret_cast<uint32_t*>(base);
-    a.chan_d = reinterpret_cast<float*>(base + L.off_d);
-    a.chan_eu = reinterpret_cast<float*>(base + L.off_eu);
     a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
     a.recs = base + L.off_recs;
-    return wkv::launch_fwd_chunked(a, dtype, nch, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+    const int io = chunk_io(dt, C, k, v, y);
+    return wkv::launch_fwd_chunked(a, io, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 }  // namespace
@@ -186,9 +158,14 @@ wkv_status wkv_forward_workspace_query(const void* ws, size_t ws_bytes, uint32_t
         return WKV_EWORKSPACE;
     const uint32_t* ctrl = reinterpret_cast<const uint32_t*>(base);
     if (hipStreamSynchronize(stream) != hipSuccess) return WKV_EHIP;
-    if (hipMemcpy(gave_up, ctrl + wkv::kCtrlGiveUp, 4, hipMemcpyDeviceToHost) != hipSuccess ||
-        hipMemcpy(epoch, ctrl + wkv::kCtrlEpoch, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    uint32_t give_up_word = 0, epoch_now = 0;
+    if (hipMemcpy(&give_up_word, ctrl + wkv::kCtrlGiveUp, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(&epoch_now, ctrl + wkv::kCtrlEpoch, 4, hipMemcpyDeviceToHost) != hipSuccess)
         return WKV_EHIP;
+    // a launch that gave up leaves its own epoch (one behind the counter) in the word
+    const uint32_t last = (epoch_now - 1u) & wkv::kCtrlEpochMask;
+    *gave_up = give_up_word == (last | wkv::kCtrlGiveUpMark) ? 1u : 0u;
+    *epoch = epoch_now;
     return WKV_OK;
 }
 

@@ -6,24 +6,25 @@
 // other op over batch and time at once and only WKV "as a scan"; the two kernels
 // here are that scan.
 //
-// Layout: k, v, y are [B, T, C] with C fastest.  A thread owns NCH consecutive
-// channels of one batch row, so a wavefront reads 64*NCH contiguous channels of
-// one time step per load (1 KiB for fp32 with NCH=4).
+// Layout: k, v, y are [B, T, C] with C fastest.  Every thread owns one channel of one
+// batch row and a wave owns 64 consecutive channels, so a wave reads one contiguous
+// segment of a time step per load.
 //
-//  * fwd_seq_kernel: each thread walks all T for its channels, L tokens at a time
+//  * fwd_seq_kernel: each thread walks all T for its channel, L tokens at a time
 //    (the chunk fast path of wkv_device.h with a per-chunk reference).
 //  * fwd_chunked_kernel: single pass over HBM.  A workgroup of NW waves owns one
-//    tile = (64*NCH channels) x (NW*L tokens); every wave keeps its L tokens of k, v
-//    in registers, reduces them to a per-wave state, the waves are combined in LDS
-//    into the tile's aggregate, and the tile's incoming state is obtained from the
-//    tiles before it by a decoupled look-back over published per-tile states (the
-//    chained-scan technique of Merrill and Garland, "Single-pass Parallel Prefix
-//    Scan with Decoupled Look-back", 2016).  Each wave then produces its outputs
-//    from its registers, so k and v are read once and y written once.
+//    tile = 64 channels x (NW*L tokens); every wave keeps its L tokens of k, v in
+//    registers, reduces them to a per-wave state, the waves are combined in LDS into
+//    the tile's aggregate, and the tile's incoming state is obtained from the tiles
+//    before it by a decoupled look-back over published per-tile states (the
+//    chained-scan technique of Merrill and Garland, "Single-pass Parallel Prefix Scan
+//    with Decoupled Look-back", 2016).  Each wave then produces its outputs from its
+//    registers, so k and v are read once and y written once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "wkv_device.h"
 #include "wkv_kernels.h"
@@ -31,7 +32,7 @@
 namespace wkv {
 
 // ----------------------------------------------------------------------------
-// Row loads and stores: NCH consecutive channels of one time step.
+// Row loads and stores: one channel per lane of one time step.
 //
 // A wave addresses its rows through a buffer resource whose base is wave-uniform
 // (scalar registers), a per-lane 32-bit byte offset (one VGPR for all rows) and a
@@ -39,42 +40,20 @@ namespace wkv {
 // ----------------------------------------------------------------------------
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base) {
     // raw buffer (stride 0), 2^31-1 addressable bytes, gfx9 data-format word
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
+// Cache policy of the k, v loads and y stores: non-temporal (nt).  Every element is
+// touched once, so keeping these lines in L2 and the MALL only evicts the look-back
+// records that are reused; measured 6.1 TB/s for a plain 12-byte-per-element stream
+// with nt against 5.7 TB/s without.
+constexpr int kStream = 2;
+
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
-template <typename IO, int NCH>
-__device__ __forceinline__ void load_row(Rsrc r, uint32_t voff, uint32_t soff, float (&o)[NCH]) {
-    if constexpr (sizeof(IO) == 4) {
-        if constexpr (NCH == 4) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-            o[0] = __uint_as_float(t.x); o[1] = __uint_as_float(t.y);
-            o[2] = __uint_as_float(t.z); o[3] = __uint_as_float(t.w);
-        } else if constexpr (NCH == 2) {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-            o[0] = __uint_as_float(t.x); o[1] = __uint_as_float(t.y);
-        } else {
-            o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-        }
-    } else {
-        if constexpr (NCH == 4) {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-            o[0] = bf_lo(t.x); o[1] = bf_hi(t.x); o[2] = bf_lo(t.y); o[3] = bf_hi(t.y);
-        } else if constexpr (NCH == 2) {
-            const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-            o[0] = bf_lo(t); o[1] = bf_hi(t);
-        } else {
-            o[0] = bf_lo((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-        }
-    }
-}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -85,65 +64,65 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-template <typename IO, int NCH>
-__device__ __forceinline__ void store_row(Rsrc r, uint32_t voff, uint32_t soff, const float (&o)[NCH]) {
-    if constexpr (sizeof(IO) == 4) {
-        if constexpr (NCH == 4) {
-            const u32x4 t = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                             __float_as_uint(o[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 0);
-        } else if constexpr (NCH == 2) {
-            const u32x2 t = {__float_as_uint(o[0]), __float_as_uint(o[1])};
-            __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, 0);
-        } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[0]), r, voff, soff, 0);
-        }
-    } else {
-        if constexpr (NCH == 4) {
-            const u32x2 t = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, 0);
-        } else if constexpr (NCH == 2) {
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(o[0], o[1]), r, voff, soff, 0);
-        } else {
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(o[0], 0.f) & 0xffffu), r,
-                                                  voff, soff, 0);
-        }
-    }
+// bfloat16 rows read and written two rows at a time: lanes 0-31 move channels (2i, 2i+1)
+// of row r and lanes 32-63 the same channels of row r+1, four bytes per lane; trading
+// words with the partner lane (lane ^ 32) then gives every lane both rows of a single
+// channel, lane i < 32 owning channel 2i and lane 32+i channel 2i+1.  A wave thus covers
+// 64 channels with 4-byte accesses and one channel per lane.  Needs an even C and
+// 4-byte aligned k, v, y.
+struct Bf16Pair {
+    uint16_t bits;
+};
+template <typename IO>
+constexpr bool kPair = std::is_same<IO, Bf16Pair>::value;
+
+// channel (within the wave's 64) of a lane in row-pair mode
+__device__ __forceinline__ int pair_channel(int lane) { return ((lane & 31) << 1) | (lane >> 5); }
+
+// Row-pair exchange, the same operation in both directions.  Load: x is the lane's word
+// of its row (channels 2i, 2i+1); the result holds the lane's own channel in rows r
+// (low half) and r+1 (high half).  Store: x holds the lane's own channel in rows r, r+1;
+// the result is the lane's word of its row.  The partner's word comes through
+// ds_bpermute (one result register, unlike a two-register swap, which kept twice the
+// in-flight words alive); v_perm_b32 then picks the halves: lanes 0-31 the low halves
+// (own word first), lanes 32-63 the high halves (partner's word first).
+__device__ __forceinline__ uint32_t pair_exchange(uint32_t x, uint32_t partner_addr, uint32_t sel) {
+    const uint32_t other = (uint32_t)__builtin_amdgcn_ds_bpermute((int)partner_addr, (int)x);
+    return __builtin_amdgcn_perm(other, x, sel);
+}
+__device__ __forceinline__ uint32_t pair_sel(uint32_t upper) { return upper ? 0x03020706u : 0x05040100u; }
+
+// One time step of this lane's channel (2-byte or 4-byte element).
+template <typename IO>
+__device__ __forceinline__ float load_elt(Rsrc r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(IO) == 4)
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream));
+    else
+        return bf_lo((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream));
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_elt(Rsrc r, uint32_t voff, uint32_t soff, float y) {
+    if constexpr (sizeof(IO) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), r, voff, soff, kStream);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(y, 0.f) & 0xffffu), r, voff,
+                                              soff, kStream);
 }
 
 // The rows of one wave: k, v, y resources based at the wave's first row and first channel.
 struct WaveRows {
     Rsrc k, v, y;
-    uint32_t lane_off;   // byte offset of this lane's first channel
-    uint32_t row_bytes;  // C * sizeof(IO)
+    uint32_t lane_off;   // byte offset of this lane's channel within a row
+    uint32_t row_bytes;  // C * element size
+    uint32_t pair_off;   // row-pair mode: byte offset of this lane's 4-byte word in a row pair
+    uint32_t upper;      // row-pair mode: 1 for lanes 32-63 (the second row of a pair)
+    uint32_t partner;    // row-pair mode: ds_bpermute address of lane ^ 32
 };
 
 // ----------------------------------------------------------------------------
-// Per-chunk arithmetic.
+// Per-token arithmetic.
 // ----------------------------------------------------------------------------
-
-// Fast path over the tokens of one chunk held in registers, from carry c (normalised)
-// with reference R: overwrites xy[j] = 2^(k_j log2e - R) with y_j and returns the state
-// after the chunk.
-template <int L, bool RAGGED>
-__device__ __forceinline__ Carry fast_outputs(const Chan& ch, const Carry& c, float R,
-                                              float (&xy)[L], const float (&v)[L], int nv) {
-    const float s = ex2((float)(c.p - (double)R));
-    float a = c.a * s, b = c.b * s;
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        if (RAGGED && j >= nv) break;
-        const float x = xy[j];
-        const float xv = x * v[j];
-        const float ex = ch.eu * x;
-        const float num = fmaf(ex, v[j], a);
-        const float den = b + ex;
-        xy[j] = num * rcp(den);
-        a = fmaf(ch.d, a, xv);
-        b = fmaf(ch.d, b, x);
-    }
-    return Carry{a, b, (double)R};
-}
 
 // One token of the exact log-sum-exp recurrence (any input, including huge exponent
 // ranges, negative w, Inf and NaN).  Returns y when OUT; advances c.
@@ -168,110 +147,271 @@ __device__ __forceinline__ float lse_token(const Chan& ch, Carry& c, float k, fl
     return y;
 }
 
-// Fallback walk over n tokens read from memory (rows t0 .. t0+n-1 at stride C), advancing
-// the NCH carries; writes y rows when yp is non-null.  Rolled loop: this path is rare and
-// keeps no chunk in registers.
-// Fallback walk over the wave's first n rows, advancing the NCH carries; writes y rows
+// Exact walk over the wave's first n rows read from memory, advancing c; writes y rows
 // when OUT and `store`.  Rolled loop: this path is rare and keeps no chunk in registers.
-template <typename IO, int NCH, bool OUT>
-__device__ __forceinline__ void lse_walk(const Chan (&ch)[NCH], Carry (&c)[NCH], const WaveRows& w,
-                                         int n, bool load, bool store) {
+template <typename IO, bool OUT>
+__device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRows& w, int n, bool load,
+                                         bool store) {
 #pragma unroll 1
     for (int j = 0; j < n; ++j) {
-        float kr[NCH], vr[NCH], yr[NCH];
         const uint32_t so = (uint32_t)j * w.row_bytes;
-        if (load) {
-            load_row<IO, NCH>(w.k, w.lane_off, so, kr);
-            load_row<IO, NCH>(w.v, w.lane_off, so, vr);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) { kr[i] = 0.f; vr[i] = 0.f; }
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) yr[i] = lse_token<OUT>(ch[i], c[i], kr[i], vr[i]);
-        if (OUT && store) store_row<IO, NCH>(w.y, w.lane_off, so, yr);
+        const float k = load ? load_elt<IO>(w.k, w.lane_off, so) : 0.f;
+        const float v = load ? load_elt<IO>(w.v, w.lane_off, so) : 0.f;
+        const float y = lse_token<OUT>(ch, c, k, v);
+        if (OUT && store) store_elt<IO>(w.y, w.lane_off, so, y);
     }
 }
 
-// Overwrite a register chunk with zeros (ends the live range of what it held).
-template <int NCH, int L>
-__device__ __forceinline__ void drop_chunk(float (&kk)[NCH][L], float (&vv)[NCH][L]) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i)
-#pragma unroll
-        for (int j = 0; j < L; ++j) { kk[i][j] = 0.f; vv[i][j] = 0.f; }
-}
+// ----------------------------------------------------------------------------
+// A wave's chunk: L consecutive tokens of k and v of this lane's channel, in registers.
+//
+// Fast path for a full, well-conditioned chunk with reference R (log2 units):
+//   x_j = 2^(k_j log2e - R),  A/2^R <- d A/2^R + x_j v_j,  y_j = (A/2^R + e^u x_j v_j)/(B/2^R + e^u x_j).
+// aggregate() gives the state of the chunk's tokens from the empty state; outputs()
+// gives the outputs from the state entering the chunk and returns the state after it.
+// ----------------------------------------------------------------------------
 
-// max and min of k over the valid tokens
-template <int L, bool RAGGED>
-__device__ __forceinline__ void k_range(const float (&k)[L], int nv, float& kmax, float& kmin) {
-    kmax = k[0];
-    kmin = k[0];
-#pragma unroll
-    for (int j = 1; j < L; ++j) {
-        if (RAGGED && j >= nv) break;
-        kmax = fmaxf(kmax, k[j]);
-        kmin = fminf(kmin, k[j]);
-    }
-}
+// float32 storage (float32 rows, or bfloat16 rows at 2 bytes per lane).  aggregate()
+// and weights() replace k by the weights x, which outputs() reuses; y replaces x.
+template <typename IO, int L>
+struct Chunk {
+    static constexpr int kStashRows = 2 * L;
+    float k[L], v[L];
 
-// Load the wave's first L rows of NCH channels; rows at or beyond nv (wave-uniform) and
-// lanes with !valid read as zero.
-template <typename IO, int NCH, int L>
-__device__ __forceinline__ void load_chunk(const WaveRows& w, int nv, bool valid,
-                                           float (&kk)[NCH][L], float (&vv)[NCH][L]) {
+    // rows at or beyond nv (wave-uniform) and lanes with !valid read as zero
+    __device__ __forceinline__ void load(const WaveRows& w, int nv, bool valid) {
 #pragma unroll
-    for (int j = 0; j < L; ++j) {
-        float kr[NCH], vr[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) { kr[i] = 0.f; vr[i] = 0.f; }
-        if (j < nv && valid) {
-            load_row<IO, NCH>(w.k, w.lane_off, (uint32_t)j * w.row_bytes, kr);
-            load_row<IO, NCH>(w.v, w.lane_off, (uint32_t)j * w.row_bytes, vr);
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) { kk[i][j] = kr[i]; vv[i][j] = vr[i]; }
-    }
-}
-
-template <typename IO, int NCH, int L>
-__device__ __forceinline__ void store_chunk(const WaveRows& w, int nv, const float (&yy)[NCH][L]) {
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        if (j < nv) {
-            float yr[NCH];
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) yr[i] = yy[i][j];
-            store_row<IO, NCH>(w.y, w.lane_off, (uint32_t)j * w.row_bytes, yr);
+        for (int j = 0; j < L; ++j) {
+            k[j] = 0.f;
+            v[j] = 0.f;
+            if (j < nv && valid) {
+                k[j] = load_elt<IO>(w.k, w.lane_off, (uint32_t)j * w.row_bytes);
+                v[j] = load_elt<IO>(w.v, w.lane_off, (uint32_t)j * w.row_bytes);
+            }
         }
     }
+    __device__ __forceinline__ void range(float& kmax, float& kmin) const {
+        kmax = k[0];
+        kmin = k[0];
+#pragma unroll
+        for (int j = 1; j < L; ++j) {
+            kmax = fmaxf(kmax, k[j]);
+            kmin = fminf(kmin, k[j]);
+        }
+    }
+    __device__ __forceinline__ Carry aggregate(const Chan& ch, float R) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const float x = ex2(fmaf(k[j], kLog2e, -R));
+            k[j] = x;
+            a = fmaf(ch.d, a, x * v[j]);
+            b = fmaf(ch.d, b, x);
+        }
+        return Carry{a, b, (double)R};
+    }
+    __device__ __forceinline__ void weights(float R) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) k[j] = ex2(fmaf(k[j], kLog2e, -R));
+    }
+    // needs the weights: call after aggregate() or weights()
+    __device__ __forceinline__ Carry outputs(const Chan& ch, const Carry& c, float R) {
+        const float s = ex2((float)(c.p - (double)R));
+        float a = c.a * s, b = c.b * s;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const float x = k[j];
+            const float xv = x * v[j];
+            const float ex = ch.eu * x;
+            const float num = fmaf(ex, v[j], a);
+            const float den = b + ex;
+            k[j] = num * rcp(den);
+            a = fmaf(ch.d, a, xv);
+            b = fmaf(ch.d, b, x);
+        }
+        return Carry{a, b, (double)R};
+    }
+    __device__ __forceinline__ void store(const WaveRows& w, bool valid) const {
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+            if (valid) store_elt<IO>(w.y, w.lane_off, (uint32_t)j * w.row_bytes, k[j]);
+    }
+    __device__ __forceinline__ void stash(uint32_t (*st)[64], int lane) const {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            st[j][lane] = __float_as_uint(k[j]);
+            st[L + j][lane] = __float_as_uint(v[j]);
+        }
+    }
+    __device__ __forceinline__ void unstash(const uint32_t (*st)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            k[j] = __uint_as_float(st[j][lane]);
+            v[j] = __uint_as_float(st[L + j][lane]);
+        }
+    }
+};
+
+// Opaque copy of a register: the compiler may not assume the value unchanged, so it
+// cannot keep values derived from the register earlier alive to reuse them later.
+__device__ __forceinline__ void reg_fence(uint32_t& x) { asm("" : "+v"(x)); }
+
+// bfloat16 row pairs, kept packed: word j holds tokens 2j (low half) and 2j+1 (high
+// half) of this lane's channel, so L tokens of k and v take L VGPRs.  The weights are
+// recomputed by outputs() (bit for bit the values aggregate() used); y replaces k,
+// packed the same way (rounded to nearest even once, from float32).  Every phase
+// unpacks again behind reg_fence(): otherwise the compiler keeps all 2L unpacked
+// floats alive between phases, which doubles the registers of a chunk.
+template <int L>
+struct Chunk<Bf16Pair, L> {
+    static_assert(L % 2 == 0, "tokens come in row pairs");
+    static constexpr int kStashRows = L;
+    uint32_t k[L / 2], v[L / 2];
+
+    __device__ __forceinline__ void fence() {
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            reg_fence(k[jj]);
+            reg_fence(v[jj]);
+        }
+    }
+
+    __device__ __forceinline__ void load(const WaveRows& w, int nv, bool valid) {
+        // every load is issued before the first exchange (which waits for its operand),
+        // and all 64 lanes reach the exchanges: only the loads are predicated
+        uint32_t xk[L / 2], xv[L / 2];
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            xk[jj] = 0u;
+            xv[jj] = 0u;
+            if (valid && 2 * jj + (int)w.upper < nv) {
+                const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
+                xk[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.k, w.pair_off, so, kStream);
+                xv[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.v, w.pair_off, so, kStream);
+            }
+        }
+        const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            k[jj] = pair_exchange(xk[jj], w.partner, sel);
+            v[jj] = pair_exchange(xv[jj], w.partner, sel);
+            // at most eight exchanges in flight, each completed in place: issuing all of
+            // them first (or sinking the byte picks to their first use) would hold a
+            // second register for every loaded word
+            if (jj % 4 == 3) {
+#pragma unroll
+                for (int q = jj - 3; q <= jj; ++q) {
+                    asm volatile("" : "+v"(k[q]));
+                    asm volatile("" : "+v"(v[q]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __device__ __forceinline__ void range(float& kmax, float& kmin) const {
+        kmax = bf_lo(k[0]);
+        kmin = kmax;
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            const float k0 = bf_lo(k[jj]), k1 = bf_hi(k[jj]);
+            kmax = fmaxf(kmax, fmaxf(k0, k1));
+            kmin = fminf(kmin, fminf(k0, k1));
+        }
+    }
+    __device__ __forceinline__ Carry aggregate(const Chan& ch, float R) {
+        fence();
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            const float x0 = ex2(fmaf(bf_lo(k[jj]), kLog2e, -R));
+            a = fmaf(ch.d, a, x0 * bf_lo(v[jj]));
+            b = fmaf(ch.d, b, x0);
+            const float x1 = ex2(fmaf(bf_hi(k[jj]), kLog2e, -R));
+            a = fmaf(ch.d, a, x1 * bf_hi(v[jj]));
+            b = fmaf(ch.d, b, x1);
+        }
+        return Carry{a, b, (double)R};
+    }
+    __device__ __forceinline__ void weights(float) {}
+    __device__ __forceinline__ Carry outputs(const Chan& ch, const Carry& c, float R) {
+        fence();
+        const float s = ex2((float)(c.p - (double)R));
+        float a = c.a * s, b = c.b * s;
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            float y[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float kf = h ? bf_hi(k[jj]) : bf_lo(k[jj]);
+                const float vf = h ? bf_hi(v[jj]) : bf_lo(v[jj]);
+                const float x = ex2(fmaf(kf, kLog2e, -R));
+                const float xv = x * vf;
+                const float ex = ch.eu * x;
+                const float num = fmaf(ex, vf, a);
+                const float den = b + ex;
+                y[h] = num * rcp(den);
+                a = fmaf(ch.d, a, xv);
+                b = fmaf(ch.d, b, x);
+            }
+            k[jj] = pack_bf16(y[0], y[1]);
+        }
+        return Carry{a, b, (double)R};
+    }
+    __device__ __forceinline__ void store(const WaveRows& w, bool valid) const {
+        // lane i < 32 writes row r (its channel and lane 32+i's), lane 32+i writes row r+1
+        const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            const uint32_t word = pair_exchange(k[jj], w.partner, sel);
+            if (valid)
+                __builtin_amdgcn_raw_buffer_store_b32(word, w.y, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
+                                                      kStream);
+        }
+    }
+    __device__ __forceinline__ void stash(uint32_t (*st)[64], int lane) const {
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            st[jj][lane] = k[jj];
+            st[L / 2 + jj][lane] = v[jj];
+        }
+    }
+    __device__ __forceinline__ void unstash(const uint32_t (*st)[64], int lane) {
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            k[jj] = st[jj][lane];
+            v[jj] = st[L / 2 + jj][lane];
+        }
+    }
+};
+
+// Tokens per lane per chunk: 32 float32 values of k and v, or 64 packed bfloat16 ones,
+// keep a chunk in 64 VGPRs.
+template <typename IO>
+constexpr int chunk_tokens() { return kPair<IO> ? 64 : 32; }
+
+// Fast-path conditions of a chunk: channel constants, the key range and the bonus stay
+// within kSpan of the reference R = max k (log2 units).
+__device__ __forceinline__ bool chunk_fast_ok(const Chan& ch, float kmax, float kmin) {
+    const float range = (kmax - kmin) * kLog2e;
+    return chan_fast_ok(ch) && (range <= kSpan) && (range - ch.u * kLog2e <= kSpan);
 }
 
 // ----------------------------------------------------------------------------
 // Sequential kernel
 // ----------------------------------------------------------------------------
 
-// grid: x covers the channels of one batch row (NCH per thread), y is the batch row.
-template <typename IO, int NCH, int L>
+// grid: x covers the channels of one batch row, y is the batch row.
+template <typename IO, int L>
 __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
     const int C = args.C, T = args.T;
     const int bi = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * NCH;
+    const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= C) return;
 
-    Chan ch[NCH];
-    Carry st[NCH];
-    bool chan_ok = true;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        ch[i] = make_chan(args.w[c + i], args.u[c + i]);
-        chan_ok = chan_ok && chan_fast_ok(ch[i]);
-        const size_t si = (size_t)bi * C + c + i;
-        st[i] = args.sin_a ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
-                           : empty_carry();
-    }
+    const Chan ch = make_chan(args.w[c], args.u[c]);
+    const size_t si = (size_t)bi * C + c;
+    Carry st = args.sin_a ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si]) : empty_carry();
     const size_t row_elems = (size_t)bi * T * C;
-    const uint32_t row_bytes = (uint32_t)(C * sizeof(IO));
 
     for (int t0 = 0; t0 < T; t0 += L) {
         const int nv = min(L, T - t0);
@@ -281,44 +421,24 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         w.v = make_rsrc(static_cast<const char*>(args.v) + off);
         w.y = make_rsrc(static_cast<char*>(args.y) + off);
         w.lane_off = (uint32_t)(c * sizeof(IO));
-        w.row_bytes = row_bytes;
-        float kk[NCH][L], vv[NCH][L];
-        load_chunk<IO, NCH, L>(w, nv, true, kk, vv);
-        float R[NCH];
-        bool ok = chan_ok && nv == L;  // the ragged last chunk walks exactly
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            float kmax, kmin;
-            k_range<L, false>(kk[i], L, kmax, kmin);
-            st[i] = normalize(st[i]);
-            R[i] = kmax * kLog2e;
-            const float range = (kmax - kmin) * kLog2e;
-            ok = ok && (range <= kSpan) && (range - ch[i].u * kLog2e <= kSpan) &&
-                 (st[i].p - (double)R[i] <= (double)kSpan);
-        }
+        w.row_bytes = (uint32_t)(C * sizeof(IO));
+        Chunk<IO, L> chunk;
+        chunk.load(w, nv, true);
+        float kmax, kmin;
+        chunk.range(kmax, kmin);
+        st = normalize(st);
+        const float R = kmax * kLog2e;
+        // the ragged last chunk walks exactly
+        const bool ok = nv == L && chunk_fast_ok(ch, kmax, kmin) && (st.p - (double)R <= (double)kSpan);
         if (__all(ok)) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-#pragma unroll
-                for (int j = 0; j < L; ++j) kk[i][j] = ex2(fmaf(kk[i][j], kLog2e, -R[i]));
-                st[i] = fast_outputs<L, false>(ch[i], st[i], R[i], kk[i], vv[i], L);
-            }
-            store_chunk<IO, NCH, L>(w, L, kk);
+            chunk.weights(R);
+            st = chunk.outputs(ch, st, R);
+            chunk.store(w, true);
         } else {
-            lse_walk<IO, NCH, true>(ch, st, w, nv, true, true);
+            lse_walk<IO, true>(ch, st, w, nv, true, true);
         }
     }
-    if (args.sout_a) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const size_t si = (size_t)bi * C + c + i;
-            float a, b, p;
-            carry_to_abi(st[i], a, b, p);
-            args.sout_a[si] = a;
-            args.sout_b[si] = b;
-            args.sout_p[si] = p;
-        }
-    }
+    if (args.sout_a) carry_to_abi(st, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
 }
 
 // ----------------------------------------------------------------------------
@@ -328,34 +448,41 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
 // Records.  Every tile publishes, per channel, two states: slot 0 the aggregate of
 // the tile alone, slot 1 the inclusive state after the tile (float32 form, see
 // rec_form).  Each of a, b, p is stored as its own 64-bit word (value | tag << 32)
-// with tag = (epoch << 2) | kind; the epoch is bumped by the prep kernel at every
-// launch, so a word belongs to this launch exactly when its tag matches.  Words are
-// written and read with device-scope atomics (single-copy atomic at 64 bits), so a
-// reader never accepts a torn or stale value and no fence or store-drain is needed.
-// A per-tile status word (the strongest kind published) lets a look-back inspect 64
-// consecutive chunks of a group in one contiguous read; it is only a hint: every
-// record word the fold consumes is re-validated by its own tag.
+// with tag = (epoch << 2) | kind; the epoch changes at every launch, so a word belongs
+// to this launch exactly when its tag matches.  Words are written and read with
+// device-scope atomics (single-copy atomic at 64 bits), so a reader never accepts a
+// torn or stale value and no fence or store-drain is needed.  A per-tile status word
+// (the strongest kind published) lets a look-back inspect 64 consecutive chunks of a
+// group in one contiguous read; it is only a hint: every record word the fold
+// consumes is re-validated by its own tag.
 //
 // Layout: status[g][chunk] (u32), so one look-back read covers 64 consecutive chunks
-// of its group, and rec[chunk][g][slot][comp][col] (u64, comp = a, b, p).  Records are
+// of its group, and rec[chunk][g][slot][comp][lane] (u64, comp = a, b, p).  Records are
 // chunk-major because the tiles in flight at any moment share a chunk index and have
 // consecutive groups: their records then form one dense region instead of landing a
 // large power-of-two stride apart, which would pile the traffic onto a few channels.
+//
+// Launch bookkeeping lives in the workspace's control block and needs no kernel of its
+// own: tiles take tickets from a counter; every workgroup counts itself done at its
+// end, and the last one resets both counters and advances the epoch for the next
+// launch (every other workgroup has read the epoch and taken its ticket by then).
 
 constexpr uint32_t kKindAgg = 1u;
 constexpr uint32_t kKindIncl = 2u;
 constexpr uint32_t kMaxSpins = 1u << 18;
-constexpr int kFoldBatch = 4;  // aggregate records loaded per round of the forward fold
+constexpr int kFoldBatch = 1;  // aggregate records loaded per round of the forward fold
+                               // (a look-back folds about one record on average; a
+                               // larger batch costs registers every tile keeps reserved)
 constexpr int kPollSleep = 2;  // s_sleep between polls (units of 64 clocks)
 
 struct TileRecs {
-    uint64_t* rec;     // records of chunk 0 of this group
-    uint32_t* status;  // this group's status words
-    int GW;
-    size_t chunk_words;  // words per chunk index over all groups: n_groups * 6 * GW
+    uint64_t* rec;       // records of chunk 0 of this group
+    uint32_t* status;    // this group's status words
+    size_t chunk_words;  // words per chunk index over all groups: n_groups * 6 * 64
     uint32_t tag_agg, tag_incl;
-    __device__ __forceinline__ uint64_t* word(int chunk, int slot, int comp, int col) const {
-        return rec + (size_t)chunk * chunk_words + (size_t)(slot * 3 + comp) * GW + col;
+    uint32_t give_up_word;  // value of the give-up word that stops this launch
+    __device__ __forceinline__ uint64_t* word(int chunk, int slot, int comp, int lane) const {
+        return rec + (size_t)chunk * chunk_words + (size_t)(slot * 3 + comp) * 64 + lane;
     }
 };
 
@@ -369,19 +496,13 @@ __device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
 __device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Publish the record of `slot` for this lane's channels, then the tile's status hint.
-template <int NCH>
-__device__ __forceinline__ void publish(const TileRecs& R, int chunk, int slot, int lane,
-                                        const Carry (&c)[NCH], uint32_t tag) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int col = lane * NCH + i;
-        st_word(R.word(chunk, slot, 0, col), c[i].a, tag);
-        st_word(R.word(chunk, slot, 1, col), c[i].b, tag);
-        st_word(R.word(chunk, slot, 2, col), (float)c[i].p, tag);
-    }
-    if (lane == 0)
-        __hip_atomic_store(&R.status[chunk], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Publish the record of `slot` for this lane's channel, then the tile's status hint.
+__device__ __forceinline__ void publish(const TileRecs& R, int chunk, int slot, int lane, const Carry& c,
+                                        uint32_t tag) {
+    st_word(R.word(chunk, slot, 0, lane), c.a, tag);
+    st_word(R.word(chunk, slot, 1, lane), c.b, tag);
+    st_word(R.word(chunk, slot, 2, lane), (float)c.p, tag);
+    if (lane == 0) __hip_atomic_store(&R.status[chunk], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The float32 form a state takes in a record: float32 reference pf and the exact
@@ -400,51 +521,44 @@ __device__ __forceinline__ Carry advance(const Carry& prev, const Carry& agg, do
     return rec_form(combine(normalize(prev), agg, decay));
 }
 
-// Raise the give-up flag (once per wave) and report failure.
-__device__ __forceinline__ bool give_up(const FwdArgs& args, int lane) {
-    if (lane == 0) atomicOr(&args.ctrl[kCtrlGiveUp], 1u);
+// Raise this launch's give-up word (once per wave) and report failure.
+__device__ __forceinline__ bool give_up(const FwdArgs& args, const TileRecs& R, int lane) {
+    if (lane == 0)
+        __hip_atomic_store(&args.ctrl[kCtrlGiveUp], R.give_up_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
 }
 
-__device__ __forceinline__ bool gave_up_elsewhere(const FwdArgs& args) {
-    return __hip_atomic_load(&args.ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+__device__ __forceinline__ bool should_stop(const FwdArgs& args, const TileRecs& R, uint32_t spin) {
+    if (spin >= kMaxSpins) return true;
+    return (spin & 31u) == 31u &&
+           __hip_atomic_load(&args.ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == R.give_up_word;
 }
 
-__device__ __forceinline__ bool should_stop(const FwdArgs& args, uint32_t spin) {
-    return spin >= kMaxSpins || ((spin & 31u) == 31u && gave_up_elsewhere(args));
-}
-
-// Read the record of (chunk, slot) for this lane's channels, re-reading until every
+// Read the record of (chunk, slot) for this lane's channel, re-reading until every
 // word carries `tag`.  Returns false after giving up.
-template <int NCH>
 __device__ __forceinline__ bool read_record(const FwdArgs& args, const TileRecs& R, int chunk, int slot,
-                                            uint32_t tag, int lane, Carry (&out)[NCH]) {
+                                            uint32_t tag, int lane, Carry& out) {
     for (uint32_t spin = 0;; ++spin) {
-        bool good = true;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int col = lane * NCH + i;
-            const uint64_t a = ld_word(R.word(chunk, slot, 0, col));
-            const uint64_t b = ld_word(R.word(chunk, slot, 1, col));
-            const uint64_t p = ld_word(R.word(chunk, slot, 2, col));
-            good = good && word_tag(a) == tag && word_tag(b) == tag && word_tag(p) == tag;
-            out[i] = Carry{word_val(a), word_val(b), (double)word_val(p)};
-        }
+        const uint64_t wa = ld_word(R.word(chunk, slot, 0, lane));
+        const uint64_t wb = ld_word(R.word(chunk, slot, 1, lane));
+        const uint64_t wp = ld_word(R.word(chunk, slot, 2, lane));
+        const bool good = word_tag(wa) == tag && word_tag(wb) == tag && word_tag(wp) == tag;
+        out = Carry{word_val(wa), word_val(wb), (double)word_val(wp)};
         if (__all(good)) return true;
-        if (should_stop(args, spin)) return give_up(args, lane);
+        if (should_stop(args, R, spin)) return give_up(args, R, lane);
         __builtin_amdgcn_s_sleep(kPollSleep);
     }
 }
 
-// Look-back for tile (chunk ci): the state entering the tile.  Lane l reads the status
-// of the chunk l+1 back until the nearest inclusive record is found with every chunk
+// The state entering chunk ci (ci >= 1): lane l inspects the status of chunk ci-1-l,
+// 64 chunks per window, until the nearest inclusive record is found with every chunk
 // after it published; the state is then folded forward from that inclusive record
-// through the aggregates in chunk order with advance(), reproducing the canonical chain
-// bit for bit.  Gives up (raising the give-up flag) after kMaxSpins polls, or soon after another
-// tile has given up, so every wave always finishes.
-template <int NCH, int TILE>
-__device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan (&ch)[NCH],
-                                          int ci, int lane, Carry (&out)[NCH]) {
+// through the aggregates in chunk order with advance(), reproducing the canonical
+// chain bit for bit.  Gives up (raising the give-up word) after kMaxSpins polls, or
+// soon after another tile has given up, so every wave always finishes.
+template <int TILE>
+__device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan& ch, int ci,
+                                          int lane, Carry& out) {
     int nearest = ci - 1;  // chunk inspected by lane 0 in the current window
     int start = -1;        // chunk holding the nearest inclusive record
     for (;;) {
@@ -452,9 +566,8 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
         const int nlanes = min(64, nearest + 1);
         bool window_done = false;
         for (uint32_t spin = 0;; ++spin) {
-            const uint32_t st = pc >= 0 ? __hip_atomic_load(&R.status[pc], __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)
-                                        : 0u;
+            const uint32_t st =
+                pc >= 0 ? __hip_atomic_load(&R.status[pc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
             const bool is_incl = pc >= 0 && st == R.tag_incl;
             const bool is_ready = is_incl || (pc >= 0 && st == R.tag_agg);
             const uint64_t incl = __ballot(is_incl);
@@ -462,238 +575,165 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
             if (incl) {
                 const int d = __builtin_ctzll(incl);
                 const uint64_t need = (d >= 63) ? ~0ull : ((2ull << d) - 1ull);
-                if ((ready & need) == need) { start = nearest - d; break; }
+                if ((ready & need) == need) {
+                    start = nearest - d;
+                    break;
+                }
             } else if (nlanes == 64 && ready == ~0ull) {
                 window_done = true;  // 64 aggregates, no inclusive record yet: look further back
                 break;
             }
-            if (should_stop(args, spin)) return give_up(args, lane);
+            if (should_stop(args, R, spin)) return give_up(args, R, lane);
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
         if (!window_done) break;
         nearest -= 64;
     }
-    Carry P[NCH];
-    if (!read_record<NCH>(args, R, start, 1, R.tag_incl, lane, P)) return false;
-    double decay[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) decay[i] = (double)TILE * w2_of(ch[i]);
+    Carry P;
+    if (!read_record(args, R, start, 1, R.tag_incl, lane, P)) return false;
+    const double decay = (double)TILE * w2_of(ch);
     // forward fold over the aggregates, kFoldBatch records per round; a round re-reads
     // its batch until every word's tag matches
 #pragma unroll 1
     for (int c0 = start + 1; c0 < ci; c0 += kFoldBatch) {
         const int n = min(kFoldBatch, ci - c0);
-        uint64_t t[kFoldBatch][NCH][3];
+        uint64_t t[kFoldBatch][3];
         for (uint32_t spin = 0;; ++spin) {
             bool good = true;
 #pragma unroll
             for (int j = 0; j < kFoldBatch; ++j)
                 if (j < n)
 #pragma unroll
-                    for (int i = 0; i < NCH; ++i)
-#pragma unroll
-                        for (int q = 0; q < 3; ++q) {
-                            t[j][i][q] = ld_word(R.word(c0 + j, 0, q, lane * NCH + i));
-                            good = good && word_tag(t[j][i][q]) == R.tag_agg;
-                        }
+                    for (int q = 0; q < 3; ++q) {
+                        t[j][q] = ld_word(R.word(c0 + j, 0, q, lane));
+                        good = good && word_tag(t[j][q]) == R.tag_agg;
+                    }
             if (__all(good)) break;
-            if (should_stop(args, spin)) return give_up(args, lane);
+            if (should_stop(args, R, spin)) return give_up(args, R, lane);
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
 #pragma unroll
         for (int j = 0; j < kFoldBatch; ++j)
             if (j < n)
-#pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    P[i] = advance(P[i],
-                                   Carry{word_val(t[j][i][0]), word_val(t[j][i][1]),
-                                         (double)word_val(t[j][i][2])},
-                                   decay[i]);
+                P = advance(P, Carry{word_val(t[j][0]), word_val(t[j][1]), (double)word_val(t[j][2])}, decay);
     }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) out[i] = P[i];
+    out = P;
     return true;
 }
 
 // Everything a tile's waves share.
-template <int NCH, int L, int NW>
+template <int NW, int STASH_ROWS>
 struct TileShared {
     int ticket;
-    float a[NW][64 * NCH];  // per-wave aggregate, then the state before each wave
-    float b[NW][64 * NCH];
-    double p[NW][64 * NCH];
-    float ca[64 * NCH];  // state entering the tile
-    float cb[64 * NCH];
-    double cp[64 * NCH];
-    float stash[2 * NCH * L][64];  // wave 0's chunk while it runs the look-back
+    float a[NW][64];  // per-wave aggregate, then the state before each wave
+    float b[NW][64];
+    double p[NW][64];
+    float ca[64];  // state entering the tile
+    float cb[64];
+    double cp[64];
+    uint32_t stash[STASH_ROWS][64];  // wave 0's chunk while it runs the look-back
 };
 
 // The tile after its k, v rows are loaded.  FAST: the wave's chunk is full and well
 // conditioned and stays in registers; otherwise the wave walks its rows in memory with
 // the exact log-sum-exp recurrence.  Both instantiations pass the same two barriers.
-template <typename IO, int NCH, int L, int NW, bool FAST>
-__device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NCH, L, NW>& sh,
-                                          const TileRecs& recs, const WaveRows& rows,
-                                          float (&kk)[NCH][L], float (&vv)[NCH][L],
-                                          const Chan (&ch)[NCH], const float (&R)[NCH], int lane,
-                                          int wid, int g, int ci, int bi, int c, bool cvalid, int nv,
-                                          int t_tile, int tile_len) {
+template <typename IO, int L, int NW, bool FAST>
+__device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Chunk<IO, L>::kStashRows>& sh,
+                                          const TileRecs& recs, const WaveRows& rows, Chunk<IO, L>& chunk,
+                                          const Chan& ch, float R, int lane, int wid, int ci, int bi, int c,
+                                          bool cvalid, int nv, int t_tile, int tile_len) {
     constexpr int TILE = L * NW;
     const int C = args.C, T = args.T;
 
     // ---- per-wave aggregate of its tokens, from the empty state ----
-    Carry agg[NCH];
+    Carry agg;
     if constexpr (FAST) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            float a = 0.f, b = 0.f;
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                const float x = ex2(fmaf(kk[i][j], kLog2e, -R[i]));
-                kk[i][j] = x;  // k is replaced by its weight relative to R
-                a = fmaf(ch[i].d, a, x * vv[i][j]);
-                b = fmaf(ch[i].d, b, x);
-            }
-            agg[i] = Carry{a, b, (double)R[i]};
-        }
+        agg = chunk.aggregate(ch, R);
     } else {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) agg[i] = empty_carry();
-        lse_walk<IO, NCH, false>(ch, agg, rows, nv, cvalid, false);
+        agg = empty_carry();
+        lse_walk<IO, false>(ch, agg, rows, nv, cvalid, false);
     }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        sh.a[wid][lane * NCH + i] = agg[i].a;
-        sh.b[wid][lane * NCH + i] = agg[i].b;
-        sh.p[wid][lane * NCH + i] = agg[i].p;
-    }
+    sh.a[wid][lane] = agg.a;
+    sh.b[wid][lane] = agg.b;
+    sh.p[wid][lane] = agg.p;
     __syncthreads();
 
     // ---- wave 0: tile aggregate, look-back, publish ----
     if (wid == 0) {
         if constexpr (FAST) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i)
-#pragma unroll
-                for (int j = 0; j < L; ++j) {
-                    sh.stash[i * L + j][lane] = kk[i][j];
-                    sh.stash[(NCH + i) * L + j][lane] = vv[i][j];
-                }
+            chunk.stash(sh.stash, lane);
             // the chunk must really leave the registers: no forwarding of the stash
             asm volatile("" ::: "memory");
         }
-        Carry run[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) run[i] = empty_carry();
+        Carry run = empty_carry();
 #pragma unroll 1
         for (int wv = 0; wv < NW; ++wv) {
             const int nvw = max(0, min(L, T - (t_tile + wv * L)));
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int col = lane * NCH + i;
-                const Carry aw{sh.a[wv][col], sh.b[wv][col], sh.p[wv][col]};
-                sh.a[wv][col] = run[i].a;  // slot wv now holds the state before wave wv
-                sh.b[wv][col] = run[i].b;
-                sh.p[wv][col] = run[i].p;
-                run[i] = combine(run[i], aw, (double)nvw * w2_of(ch[i]));
-            }
+            const Carry aw{sh.a[wv][lane], sh.b[wv][lane], sh.p[wv][lane]};
+            sh.a[wv][lane] = run.a;  // slot wv now holds the state before wave wv
+            sh.b[wv][lane] = run.b;
+            sh.p[wv][lane] = run.p;
+            run = combine(run, aw, (double)nvw * w2_of(ch));
         }
-        Carry agg_rec[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) agg_rec[i] = rec_form(run[i]);
-        Carry prefix[NCH];
+        const Carry agg_rec = rec_form(run);
+        Carry prefix;
         if (ci == 0) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const size_t si = (size_t)bi * C + c + i;
-                prefix[i] = rec_form((args.sin_a && cvalid)
-                                         ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
-                                         : empty_carry());
-            }
+            const size_t si = (size_t)bi * C + c;
+            prefix = rec_form((args.sin_a && cvalid) ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
+                                                      : empty_carry());
         } else {
-            publish<NCH>(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-            if (!look_back<NCH, TILE>(args, recs, ch, ci, lane, prefix)) {
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) prefix[i] = empty_carry();
-            }
+            publish(recs, ci, 0, lane, agg_rec, recs.tag_agg);
+            if (!look_back<TILE>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
         }
-        Carry incl[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-            incl[i] = advance(prefix[i], agg_rec[i], (double)tile_len * w2_of(ch[i]));
+        const Carry incl = advance(prefix, agg_rec, (double)tile_len * w2_of(ch));
         if (ci + 1 < args.n_chunks) {
-            publish<NCH>(recs, ci, 1, lane, incl, recs.tag_incl);
+            publish(recs, ci, 1, lane, incl, recs.tag_incl);
         } else if (args.sout_a && cvalid) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const size_t si = (size_t)bi * C + c + i;
-                float a, b, p;
-                carry_to_abi(incl[i], a, b, p);
-                args.sout_a[si] = a;
-                args.sout_b[si] = b;
-                args.sout_p[si] = p;
-            }
+            const size_t si = (size_t)bi * C + c;
+            carry_to_abi(incl, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
         }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            sh.ca[lane * NCH + i] = prefix[i].a;
-            sh.cb[lane * NCH + i] = prefix[i].b;
-            sh.cp[lane * NCH + i] = prefix[i].p;
-        }
+        sh.ca[lane] = prefix.a;
+        sh.cb[lane] = prefix.b;
+        sh.cp[lane] = prefix.p;
         if constexpr (FAST) {
             asm volatile("" ::: "memory");
-#pragma unroll
-            for (int i = 0; i < NCH; ++i)
-#pragma unroll
-                for (int j = 0; j < L; ++j) {
-                    kk[i][j] = sh.stash[i * L + j][lane];
-                    vv[i][j] = sh.stash[(NCH + i) * L + j][lane];
-                }
+            chunk.unstash(sh.stash, lane);
         }
     }
     __syncthreads();
     if (nv == 0) return;
 
     // ---- outputs of this wave from the state entering its tokens ----
-    Carry cin[NCH];
-    bool out_ok = FAST;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int col = lane * NCH + i;
-        const Carry tile_in{sh.ca[col], sh.cb[col], sh.cp[col]};
-        const Carry before{sh.a[wid][col], sh.b[wid][col], sh.p[wid][col]};
-        cin[i] = normalize(combine(tile_in, before, (double)(wid * L) * w2_of(ch[i])));
-        out_ok = out_ok && (cin[i].p - (double)R[i] <= (double)kSpan);
-    }
-    if (FAST && __all(out_ok)) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) fast_outputs<L, false>(ch[i], cin[i], R[i], kk[i], vv[i], L);
-        if (cvalid) store_chunk<IO, NCH, L>(rows, L, kk);
+    const Carry tile_in{sh.ca[lane], sh.cb[lane], sh.cp[lane]};
+    const Carry before{sh.a[wid][lane], sh.b[wid][lane], sh.p[wid][lane]};
+    const Carry cin = normalize(combine(tile_in, before, (double)(wid * L) * w2_of(ch)));
+    if (FAST && __all(cin.p - (double)R <= (double)kSpan)) {
+        chunk.outputs(ch, cin, R);
+        chunk.store(rows, cvalid);
     } else {
-        lse_walk<IO, NCH, true>(ch, cin, rows, nv, cvalid, cvalid);
+        Carry c2 = cin;
+        lse_walk<IO, true>(ch, c2, rows, nv, cvalid, cvalid);
     }
 }
 
-template <typename IO, int NCH, int L, int NW>
+template <typename IO, int L, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
-    constexpr int GW = 64 * NCH;
     constexpr int TILE = L * NW;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
     const int C = args.C, T = args.T;
-    __shared__ TileShared<NCH, L, NW> sh;
+    __shared__ TileShared<NW, Chunk<IO, L>::kStashRows> sh;
 
     // Tiles are numbered in the order workgroups start, so every tile this one waits on
     // has already started and publishes its aggregate without waiting for anything.
     if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
     const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
-    const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
     const int g = ticket % args.n_groups;
     const int ci = ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
-    const int c_grp = (g - bi * args.groups_per_row) * GW;
-    const int c = c_grp + lane * NCH;
+    const int c_grp = (g - bi * args.groups_per_row) * 64;
+    const int c = c_grp + (kPair<IO> ? pair_channel(lane) : lane);
     const bool cvalid = c < C;
     const int t_tile = ci * TILE;
     const int t0 = __builtin_amdgcn_readfirstlane(t_tile + wid * L);
@@ -706,61 +746,50 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
         rows.k = make_rsrc(static_cast<const char*>(args.k) + off);
         rows.v = make_rsrc(static_cast<const char*>(args.v) + off);
         rows.y = make_rsrc(static_cast<char*>(args.y) + off);
-        rows.lane_off = (uint32_t)(lane * NCH * sizeof(IO));
+        rows.lane_off = (uint32_t)((c - c_grp) * sizeof(IO));
         rows.row_bytes = (uint32_t)(C * sizeof(IO));
+        rows.pair_off = (uint32_t)((lane & 31) * 4) + (uint32_t)(lane >> 5) * rows.row_bytes;
+        rows.upper = (uint32_t)(lane >> 5);
+        rows.partner = (uint32_t)((lane ^ 32) << 2);
     }
+    Chunk<IO, L> chunk;
+    chunk.load(rows, nv, cvalid);
+
+    // read after the loads are issued; constant during the launch
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
     TileRecs recs;
-    recs.rec = static_cast<uint64_t*>(args.recs) + (size_t)g * 6 * GW;
-    recs.chunk_words = (size_t)args.n_groups * 6 * GW;
+    recs.rec = static_cast<uint64_t*>(args.recs) + (size_t)g * 6 * 64;
+    recs.chunk_words = (size_t)args.n_groups * 6 * 64;
     recs.status = args.status + (size_t)g * args.n_chunks;
-    recs.GW = GW;
     recs.tag_agg = (epoch << 2) | kKindAgg;
     recs.tag_incl = (epoch << 2) | kKindIncl;
+    recs.give_up_word = epoch | kCtrlGiveUpMark;
 
-    float kk[NCH][L], vv[NCH][L];
-    load_chunk<IO, NCH, L>(rows, nv, cvalid, kk, vv);
-
-    Chan ch[NCH];
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int ci_ = cvalid ? c + i : 0;
-        ch[i] = Chan{args.chan_d[ci_], args.chan_eu[ci_], args.w[ci_], args.u[ci_]};
-        ok = ok && chan_fast_ok(ch[i]);
-    }
-    float R[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        float kmax, kmin;
-        k_range<L, false>(kk[i], L, kmax, kmin);
-        R[i] = kmax * kLog2e;
-        const float range = (kmax - kmin) * kLog2e;
-        ok = ok && (range <= kSpan) && (range - ch[i].u * kLog2e <= kSpan);
-    }
+    const int cw = cvalid ? c : 0;
+    const Chan ch = make_chan(args.w[cw], args.u[cw]);
+    float kmax, kmin;
+    chunk.range(kmax, kmin);
+    const float R = kmax * kLog2e;
     // the fast path takes full chunks only; the one ragged chunk at the end of a
     // sequence (and any ill-conditioned chunk) walks its rows exactly
-    if (__all(ok) && nv == L)
-        tile_body<IO, NCH, L, NW, true>(args, sh, recs, rows, kk, vv, ch, R, lane, wid, g, ci, bi, c,
-                                        cvalid, nv, t_tile, tile_len);
+    if (__all(chunk_fast_ok(ch, kmax, kmin)) && nv == L)
+        tile_body<IO, L, NW, true>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv, t_tile,
+                                   tile_len);
     else
-        tile_body<IO, NCH, L, NW, false>(args, sh, recs, rows, kk, vv, ch, R, lane, wid, g, ci, bi, c,
-                                         cvalid, nv, t_tile, tile_len);
-}
+        tile_body<IO, L, NW, false>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv, t_tile,
+                                    tile_len);
 
-// Per launch: reset the ticket counter and give-up flag, open a new record epoch, and
-// compute the per-channel constants e^{-w} and e^{u} once (float64 exp, rounded).
-__global__ void prep_kernel(uint32_t* __restrict__ ctrl, const float* __restrict__ w,
-                            const float* __restrict__ u, float* __restrict__ cd,
-                            float* __restrict__ ceu, int C) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) {
-        ctrl[kCtrlTicket] = 0u;
-        ctrl[kCtrlGiveUp] = 0u;
-        ctrl[kCtrlEpoch] = (ctrl[kCtrlEpoch] + 1u) & 0x3fffffffu;
-    }
-    if (i < C) {
-        cd[i] = (float)exp(-(double)w[i]);
-        ceu[i] = (float)exp((double)u[i]);
+    // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t n_tiles = (uint32_t)args.n_groups * (uint32_t)args.n_chunks;
+        const uint32_t done = atomicAdd(&args.ctrl[kCtrlDone], 1u);
+        if (done + 1u == n_tiles) {
+            __hip_atomic_store(&args.ctrl[kCtrlTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&args.ctrl[kCtrlDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&args.ctrl[kCtrlEpoch], (epoch + 1u) & kCtrlEpochMask, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -772,8 +801,8 @@ __global__ void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
 
 // State copy used when T = 0 and the caller asked for the state through.
 __global__ void copy_state_kernel(const float* __restrict__ ia, const float* __restrict__ ib,
-                                  const float* __restrict__ ip, float* __restrict__ oa,
-                                  float* __restrict__ ob, float* __restrict__ op, long n) {
+                                  const float* __restrict__ ip, float* __restrict__ oa, float* __restrict__ ob,
+                                  float* __restrict__ op, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     oa[i] = ia ? ia[i] : 0.f;
@@ -785,68 +814,67 @@ __global__ void copy_state_kernel(const float* __restrict__ ia, const float* __r
 // Launchers
 // ----------------------------------------------------------------------------
 
-// Tokens per thread per chunk: NCH * L = 32 keeps k and v of a chunk in 64 VGPRs.
-template <int NCH>
-constexpr int chunk_tokens() { return 32 / NCH; }
-
-template <typename IO, int NCH>
-static hipError_t launch_seq_t(const FwdArgs& a, hipStream_t s) {
-    constexpr int L = chunk_tokens<NCH>();
-    const long per_row = a.C / NCH;
-    const long blocks = (per_row + 255) / 256;
-    hipLaunchKernelGGL((fwd_seq_kernel<IO, NCH, L>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256),
-                       0, s, a);
-    return hipGetLastError();
-}
-
-// Channels per thread: only NCH = 1 is instantiated at present (wider rows raise the
-// register count past four waves per SIMD).
-hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, int nch, hipStream_t s) {
-    if (nch != 1) return hipErrorInvalidValue;
-    return dtype == 0 ? launch_seq_t<float, 1>(a, s) : launch_seq_t<uint16_t, 1>(a, s);
-}
-
-template <typename IO, int NCH, int NW>
-static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
-    constexpr int L = chunk_tokens<NCH>();
-    const long n_tiles = (long)a.n_groups * a.n_chunks;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((a.C + 255) / 256)), dim3(256), 0, s, a.ctrl, a.w,
-                       a.u, a.chan_d, a.chan_eu, a.C);
-    hipLaunchKernelGGL((fwd_chunked_kernel<IO, NCH, L, NW>), dim3((unsigned)n_tiles), dim3(64 * NW),
-                       0, s, a);
-    return hipGetLastError();
-}
-
-// Tile = NW waves x (32 / NCH) tokens.
 template <typename IO>
-static hipError_t launch_chunked_n(const FwdArgs& a, int nch, int tile, hipStream_t s) {
-    if (nch == 2) {
-        if (tile == 64) return launch_chunked_t<IO, 2, 4>(a, s);
-        if (tile == 128) return launch_chunked_t<IO, 2, 8>(a, s);
-        if (tile == 256) return launch_chunked_t<IO, 2, 16>(a, s);
-    } else if (nch == 1) {
-        if (tile == 64) return launch_chunked_t<IO, 1, 2>(a, s);
-        if (tile == 128) return launch_chunked_t<IO, 1, 4>(a, s);
-        if (tile == 256) return launch_chunked_t<IO, 1, 8>(a, s);
+static hipError_t launch_seq_t(const FwdArgs& a, hipStream_t s) {
+    const long blocks = (a.C + 255) / 256;
+    hipLaunchKernelGGL((fwd_seq_kernel<IO, 32>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_seq_t<float>(a, s) : launch_seq_t<uint16_t>(a, s);
+}
+
+template <typename IO, int NW>
+static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
+    constexpr int L = chunk_tokens<IO>();
+    const long n_tiles = (long)a.n_groups * a.n_chunks;
+    hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+// Tile = NW waves x chunk_tokens tokens, 64 channels; at most 16 waves (1024 threads).
+template <typename IO>
+static hipError_t launch_chunked_n(const FwdArgs& a, int tile, hipStream_t s) {
+    constexpr int L = chunk_tokens<IO>();
+    if constexpr (L == 64) {
+        switch (tile) {
+            case 64: return launch_chunked_t<IO, 1>(a, s);
+            case 128: return launch_chunked_t<IO, 2>(a, s);
+            case 256: return launch_chunked_t<IO, 4>(a, s);
+            case 512: return launch_chunked_t<IO, 8>(a, s);
+        }
+    } else {
+        switch (tile) {
+            case 64: return launch_chunked_t<IO, 2>(a, s);
+            case 128: return launch_chunked_t<IO, 4>(a, s);
+            case 256: return launch_chunked_t<IO, 8>(a, s);
+            case 512: return launch_chunked_t<IO, 16>(a, s);
+        }
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_chunked(const FwdArgs& a, int dtype, int nch, int tile, hipStream_t s) {
-    return dtype == 0 ? launch_chunked_n<float>(a, nch, tile, s) : launch_chunked_n<uint16_t>(a, nch, tile, s);
+hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s) {
+    switch (io) {
+        case kIoF32: return launch_chunked_n<float>(a, tile, s);
+        case kIoBf16: return launch_chunked_n<uint16_t>(a, tile, s);
+        case kIoBf16Pair: return launch_chunked_n<Bf16Pair>(a, tile, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s) {
     const size_t blocks = std::min<size_t>(4096, (n_words + 255) / 256 + 1);
-    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<uint32_t*>(p), n_words);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                       n_words);
     return hipGetLastError();
 }
 
-hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
-                             float* ob, float* op, long n, hipStream_t s) {
-    hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ia, ib,
-                       ip, oa, ob, op, n);
+hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa, float* ob, float* op,
+                             long n, hipStream_t s) {
+    hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ia, ib, ip, oa, ob,
+                       op, n);
     return hipGetLastError();
 }
 

@@ -6,13 +6,17 @@
 
 namespace wkv {
 
-// Control block at the start of a chunked workspace.  The ticket counter takes every
-// workgroup's atomic add, so it sits alone in its cache line: a plain read of a word
-// sharing that line queues behind the atomics and stalls the reading tile.
-constexpr int kCtrlTicket = 0;   // tile ticket counter (reset per launch)
-constexpr int kCtrlEpoch = 32;   // record epoch (bumped per launch), 128 bytes in
-constexpr int kCtrlGiveUp = 48;  // look-back give-up flag (reset per launch)
-constexpr int kCtrlWords = 64;   // 256 bytes
+// Control block at the start of a chunked workspace (zero-filled before first use).
+// The ticket and done counters take every workgroup's atomic add, so each sits alone
+// in its cache line: a plain read of a word sharing such a line queues behind the
+// atomics and stalls the reading tile.
+constexpr int kCtrlTicket = 0;   // tile ticket counter (zero between launches)
+constexpr int kCtrlEpoch = 32;   // record epoch: number of completed launches, mod 2^30
+constexpr int kCtrlGiveUp = 48;  // (epoch | kCtrlGiveUpMark) once a launch gave up waiting
+constexpr int kCtrlDone = 64;    // workgroups finished in the current launch
+constexpr int kCtrlWords = 128;  // 512 bytes
+constexpr uint32_t kCtrlEpochMask = 0x3fffffffu;
+constexpr uint32_t kCtrlGiveUpMark = 0x40000000u;
 
 // Arguments of the forward kernels (plain pointers; see include/libwkv.h for meaning).
 struct FwdArgs {
@@ -28,20 +32,23 @@ struct FwdArgs {
     float* sout_b;
     float* sout_p;
     // chunked algorithm only (workspace carve-up)
-    uint32_t* ctrl;  // control block, kCtrlWords words (see below)
-    float* chan_d;   // [C] e^{-w}, written by the prep kernel
-    float* chan_eu;  // [C] e^{u}
+    uint32_t* ctrl;  // control block, kCtrlWords words
     uint32_t* status;  // [n_groups][n_chunks] status hints
-    void* recs;        // [n_chunks][n_groups][2][3][64 * NCH] tagged 64-bit words
+    void* recs;        // [n_chunks][n_groups][2][3][64] tagged 64-bit words
     int B, T, C;
-    int groups_per_row;  // ceil(C / (64 * NCH))
+    int groups_per_row;  // ceil(C / 64)
     int n_groups;        // B * groups_per_row
     int n_chunks;        // ceil(T / tile)
 };
 
-// dtype: 0 = float32, 1 = bfloat16.  nch: channels per thread (1, 2 or 4).
-hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, int nch, hipStream_t s);
-hipError_t launch_fwd_chunked(const FwdArgs& a, int dtype, int nch, int tile, hipStream_t s);
+// How the chunked kernel moves k, v, y: float32 rows; bfloat16 rows at 2 bytes per lane;
+// bfloat16 row pairs at 4 bytes per lane (even C, 4-byte aligned k, v, y).
+enum IoMode { kIoF32 = 0, kIoBf16 = 1, kIoBf16Pair = 2 };
+
+// dtype: 0 = float32, 1 = bfloat16.
+hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s);
+// tile: 64, 128, 256 or 512 time steps per workgroup (one channel per lane, 64 per group).
+hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s);
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
                              float* ob, float* op, long n, hipStream_t s);
