@@ -42,6 +42,14 @@ int resolve_algo(wkv_algo algo, int64_t B, int64_t T, int64_t C) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Chunk length when the caller passes 0: 256, or 512 for problems of fewer than 1024
+// tiles of 256, where the per-tile look-back dominates (B=8, T=1024, C=768 float32:
+// 20 us at 512 against 25 us at 256).
+int default_tile(int64_t B, int64_t T, int64_t C) {
+    const int64_t tiles = B * ceil_div(C, 64) * ceil_div(T, kDefaultTile);
+    return tiles < 1024 ? 2 * kDefaultTile : kDefaultTile;
+}
+
 // Workspace of the chunked algorithm: [control words][status word per tile][records: per
 // tile and channel, two states of three tagged 64-bit words].
 struct ChunkLayout {
@@ -114,7 +122,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
         return wkv::launch_fwd_seq(a, dtype, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
     }
 
-    const int tile = chunk_len ? (int)chunk_len : kDefaultTile;
+    const int tile = chunk_len ? (int)chunk_len : default_tile(B, T, C);
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
     a.groups_per_row = (int)ceil_div(C, 64);
@@ -141,7 +149,7 @@ size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt
     if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return (size_t)-1;
     if (B == 0 || T == 0 || C == 0) return 0;
     if (resolve_algo(algo, B, T, C) == WKV_ALGO_SEQ) return 0;
-    return chunked_bytes_bound(B, T, C, chunk_len ? (int)chunk_len : kDefaultTile);
+    return chunked_bytes_bound(B, T, C, chunk_len ? (int)chunk_len : default_tile(B, T, C));
 }
 
 wkv_status wkv_forward_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {

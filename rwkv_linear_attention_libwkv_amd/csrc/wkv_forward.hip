@@ -166,7 +166,8 @@ __device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRow
 // A wave's chunk: L consecutive tokens of k and v of this lane's channel, in registers.
 //
 // Fast path for a full, well-conditioned chunk with reference R (log2 units):
-//   x_j = 2^(k_j log2e - R),  A/2^R <- d A/2^R + x_j v_j,  y_j = (A/2^R + e^u x_j v_j)/(B/2^R + e^u x_j).
+//   x_j = 2^(k_j log2e - R),  y_j = (A/2^R + e^u x_j v_j)/(B/2^R + e^u x_j),  A/2^R <- d A/2^R + x_j v_j
+// (and B likewise), with y_j formed as fma(e^u, x_j v_j, A/2^R) * rcp(fma(e^u, x_j, B/2^R)).
 // aggregate() gives the state of the chunk's tokens from the empty state; outputs()
 // gives the outputs from the state entering the chunk and returns the state after it.
 // ----------------------------------------------------------------------------
@@ -222,10 +223,7 @@ struct Chunk {
         for (int j = 0; j < L; ++j) {
             const float x = k[j];
             const float xv = x * v[j];
-            const float ex = ch.eu * x;
-            const float num = fmaf(ex, v[j], a);
-            const float den = b + ex;
-            k[j] = num * rcp(den);
+            k[j] = fmaf(ch.eu, xv, a) * rcp(fmaf(ch.eu, x, b));
             a = fmaf(ch.d, a, xv);
             b = fmaf(ch.d, b, x);
         }
@@ -346,10 +344,7 @@ struct Chunk<Bf16Pair, L> {
                 const float vf = h ? bf_hi(v[jj]) : bf_lo(v[jj]);
                 const float x = ex2(fmaf(kf, kLog2e, -R));
                 const float xv = x * vf;
-                const float ex = ch.eu * x;
-                const float num = fmaf(ex, vf, a);
-                const float den = b + ex;
-                y[h] = num * rcp(den);
+                y[h] = fmaf(ch.eu, xv, a) * rcp(fmaf(ch.eu, x, b));
                 a = fmaf(ch.d, a, xv);
                 b = fmaf(ch.d, b, x);
             }

@@ -20,6 +20,11 @@
 
 namespace wkv {
 
+// Every array except w and u is touched once per step: those accesses are non-temporal
+// (nt), so they do not evict w and u (shared by the N sequences) from the caches.
+typedef float vf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int vu32x2 __attribute__((ext_vector_type(2)));
+
 template <int NCH>
 __device__ __forceinline__ void ld4(const float* __restrict__ p, float (&o)[NCH]) {
     if constexpr (NCH == 4) {
@@ -32,34 +37,46 @@ __device__ __forceinline__ void ld4(const float* __restrict__ p, float (&o)[NCH]
 }
 
 template <int NCH>
-__device__ __forceinline__ void st4(float* __restrict__ p, const float (&o)[NCH]) {
+__device__ __forceinline__ void ld4_nt(const float* __restrict__ p, float (&o)[NCH]) {
     if constexpr (NCH == 4) {
-        *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+        const vf32x4 t = __builtin_nontemporal_load(reinterpret_cast<const vf32x4*>(p));
+        o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
     } else {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) p[i] = o[i];
+        for (int i = 0; i < NCH; ++i) o[i] = __builtin_nontemporal_load(p + i);
     }
 }
 
 template <int NCH>
-__device__ __forceinline__ void ld_io(const float* __restrict__ p, float (&o)[NCH]) { ld4<NCH>(p, o); }
+__device__ __forceinline__ void st4_nt(float* __restrict__ p, const float (&o)[NCH]) {
+    if constexpr (NCH == 4) {
+        const vf32x4 t = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(t, reinterpret_cast<vf32x4*>(p));
+    } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) __builtin_nontemporal_store(o[i], p + i);
+    }
+}
+
+template <int NCH>
+__device__ __forceinline__ void ld_io(const float* __restrict__ p, float (&o)[NCH]) { ld4_nt<NCH>(p, o); }
 
 template <int NCH>
 __device__ __forceinline__ void ld_io(const uint16_t* __restrict__ p, float (&o)[NCH]) {
     if constexpr (NCH == 4) {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        const vu32x2 t = __builtin_nontemporal_load(reinterpret_cast<const vu32x2*>(p));
         o[0] = __uint_as_float(t.x << 16);
         o[1] = __uint_as_float(t.x & 0xffff0000u);
         o[2] = __uint_as_float(t.y << 16);
         o[3] = __uint_as_float(t.y & 0xffff0000u);
     } else {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) o[i] = __uint_as_float((uint32_t)p[i] << 16);
+        for (int i = 0; i < NCH; ++i) o[i] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p + i) << 16);
     }
 }
 
 template <int NCH>
-__device__ __forceinline__ void st_io(float* __restrict__ p, const float (&o)[NCH]) { st4<NCH>(p, o); }
+__device__ __forceinline__ void st_io(float* __restrict__ p, const float (&o)[NCH]) { st4_nt<NCH>(p, o); }
 
 typedef float sf32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 sbf16x2 __attribute__((ext_vector_type(2)));
@@ -72,10 +89,12 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 template <int NCH>
 __device__ __forceinline__ void st_io(uint16_t* __restrict__ p, const float (&o)[NCH]) {
     if constexpr (NCH == 4) {
-        *reinterpret_cast<uint2*>(p) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+        const vu32x2 t = {pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+        __builtin_nontemporal_store(t, reinterpret_cast<vu32x2*>(p));
     } else {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) p[i] = (uint16_t)(pack2_bf16(o[i], 0.f) & 0xffffu);
+        for (int i = 0; i < NCH; ++i)
+            __builtin_nontemporal_store((uint16_t)(pack2_bf16(o[i], 0.f) & 0xffffu), p + i);
     }
 }
 
@@ -91,9 +110,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs args) {
     ld4<NCH>(args.u + wi, u);
     ld_io<NCH>(static_cast<const IO*>(args.k) + li, k);
     ld_io<NCH>(static_cast<const IO*>(args.v) + li, v);
-    ld4<NCH>(args.a + li, a);
-    ld4<NCH>(args.b + li, b);
-    ld4<NCH>(args.p + li, p);
+    ld4_nt<NCH>(args.a + li, a);
+    ld4_nt<NCH>(args.b + li, b);
+    ld4_nt<NCH>(args.p + li, p);
 
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -117,9 +136,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs args) {
         p[i] = pn;
     }
     st_io<NCH>(static_cast<IO*>(args.y) + li, y);
-    st4<NCH>(args.a + li, a);
-    st4<NCH>(args.b + li, b);
-    st4<NCH>(args.p + li, p);
+    st4_nt<NCH>(args.a + li, a);
+    st4_nt<NCH>(args.b + li, b);
+    st4_nt<NCH>(args.p + li, p);
 }
 
 template <typename IO, int NCH>
