@@ -66,9 +66,7 @@ ChunkLayout chunked_layout(int64_t B, int64_t T, int64_t C, int tile) {
     return L;
 }
 
-size_t chunked_bytes_bound(int64_t B, int64_t T, int64_t C, int tile) {
-    return chunked_layout(B, T, C, tile).total;
-}
+size_t chunked_bytes_bound(int64_t B, int64_t T, int64_t C, int tile) { return chunked_layout(B, T, C, tile).total; }
 
 bool sizes_ok(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0) return false;
@@ -125,6 +123,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     const int tile = chunk_len ? (int)chunk_len : default_tile(B, T, C);
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
+    const int io = chunk_io(dt, C, k, v, y);
     a.groups_per_row = (int)ceil_div(C, 64);
     a.n_groups = (int)(B * a.groups_per_row);
     a.n_chunks = (int)ceil_div(T, tile);
@@ -135,7 +134,6 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.ctrl = reinterpret_cast<uint32_t*>(base);
     a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
     a.recs = base + L.off_recs;
-    const int io = chunk_io(dt, C, k, v, y);
     return wkv::launch_fwd_chunked(a, io, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 

@@ -172,6 +172,57 @@ __device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRow
 // gives the outputs from the state entering the chunk and returns the state after it.
 // ----------------------------------------------------------------------------
 
+// Load L rows of k and v in row-pair mode into packed words (word j: tokens 2j, 2j+1 of
+// this lane's channel).  Rows at or beyond nv and lanes with !valid read as zero.
+template <int L>
+__device__ __forceinline__ void load_pairs(const WaveRows& w, int nv, bool valid, uint32_t (&k)[L / 2],
+                                           uint32_t (&v)[L / 2]) {
+    // every load is issued before the first exchange (which waits for its operand),
+    // and all 64 lanes reach the exchanges: only the loads are predicated
+    uint32_t xk[L / 2], xv[L / 2];
+#pragma unroll
+    for (int jj = 0; jj < L / 2; ++jj) {
+        xk[jj] = 0u;
+        xv[jj] = 0u;
+        if (valid && 2 * jj + (int)w.upper < nv) {
+            const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
+            xk[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.k, w.pair_off, so, kStream);
+            xv[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.v, w.pair_off, so, kStream);
+        }
+    }
+    const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+    for (int jj = 0; jj < L / 2; ++jj) {
+        k[jj] = pair_exchange(xk[jj], w.partner, sel);
+        v[jj] = pair_exchange(xv[jj], w.partner, sel);
+        // at most eight exchanges in flight, each completed in place: issuing all of
+        // them first (or sinking the byte picks to their first use) would hold a
+        // second register for every loaded word
+        if (jj % 4 == 3) {
+#pragma unroll
+            for (int q = jj - 3; q <= jj; ++q) {
+                asm volatile("" : "+v"(k[q]));
+                asm volatile("" : "+v"(v[q]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Store L rows of y held as packed words in row-pair mode.
+template <int L>
+__device__ __forceinline__ void store_pairs(const WaveRows& w, bool valid, const uint32_t (&y)[L / 2]) {
+    // lane i < 32 writes row r (its channel and lane 32+i's), lane 32+i writes row r+1
+    const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+    for (int jj = 0; jj < L / 2; ++jj) {
+        const uint32_t word = pair_exchange(y[jj], w.partner, sel);
+        if (valid)
+            __builtin_amdgcn_raw_buffer_store_b32(word, w.y, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
+                                                  kStream);
+    }
+}
+
 // float32 storage (float32 rows, or bfloat16 rows at 2 bytes per lane).  aggregate()
 // and weights() replace k by the weights x, which outputs() reuses; y replaces x.
 template <typename IO, int L>
@@ -274,38 +325,7 @@ struct Chunk<Bf16Pair, L> {
         }
     }
 
-    __device__ __forceinline__ void load(const WaveRows& w, int nv, bool valid) {
-        // every load is issued before the first exchange (which waits for its operand),
-        // and all 64 lanes reach the exchanges: only the loads are predicated
-        uint32_t xk[L / 2], xv[L / 2];
-#pragma unroll
-        for (int jj = 0; jj < L / 2; ++jj) {
-            xk[jj] = 0u;
-            xv[jj] = 0u;
-            if (valid && 2 * jj + (int)w.upper < nv) {
-                const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
-                xk[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.k, w.pair_off, so, kStream);
-                xv[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.v, w.pair_off, so, kStream);
-            }
-        }
-        const uint32_t sel = pair_sel(w.upper);
-#pragma unroll
-        for (int jj = 0; jj < L / 2; ++jj) {
-            k[jj] = pair_exchange(xk[jj], w.partner, sel);
-            v[jj] = pair_exchange(xv[jj], w.partner, sel);
-            // at most eight exchanges in flight, each completed in place: issuing all of
-            // them first (or sinking the byte picks to their first use) would hold a
-            // second register for every loaded word
-            if (jj % 4 == 3) {
-#pragma unroll
-                for (int q = jj - 3; q <= jj; ++q) {
-                    asm volatile("" : "+v"(k[q]));
-                    asm volatile("" : "+v"(v[q]));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    }
+    __device__ __forceinline__ void load(const WaveRows& w, int nv, bool valid) { load_pairs<L>(w, nv, valid, k, v); }
     __device__ __forceinline__ void range(float& kmax, float& kmin) const {
         kmax = bf_lo(k[0]);
         kmin = kmax;
@@ -352,17 +372,7 @@ struct Chunk<Bf16Pair, L> {
         }
         return Carry{a, b, (double)R};
     }
-    __device__ __forceinline__ void store(const WaveRows& w, bool valid) const {
-        // lane i < 32 writes row r (its channel and lane 32+i's), lane 32+i writes row r+1
-        const uint32_t sel = pair_sel(w.upper);
-#pragma unroll
-        for (int jj = 0; jj < L / 2; ++jj) {
-            const uint32_t word = pair_exchange(k[jj], w.partner, sel);
-            if (valid)
-                __builtin_amdgcn_raw_buffer_store_b32(word, w.y, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
-                                                      kStream);
-        }
-    }
+    __device__ __forceinline__ void store(const WaveRows& w, bool valid) const { store_pairs<L>(w, valid, k); }
     __device__ __forceinline__ void stash(uint32_t (*st)[64], int lane) const {
 #pragma unroll
         for (int jj = 0; jj < L / 2; ++jj) {
@@ -465,9 +475,13 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
 constexpr uint32_t kKindAgg = 1u;
 constexpr uint32_t kKindIncl = 2u;
 constexpr uint32_t kMaxSpins = 1u << 18;
-constexpr int kFoldBatch = 1;  // aggregate records loaded per round of the forward fold
-                               // (a look-back folds about one record on average; a
-                               // larger batch costs registers every tile keeps reserved)
+// Aggregate records a look-back loads per round of its forward fold.  Registers for the
+// batch are reserved by every wave (the look-back's code path shares the allocation with
+// the waves that keep their chunk), so the batch is one record: float32 tiles fold 0.3
+// records on average (B=8, T=8192, C=2048) and packed bfloat16 tiles 1.6 (B=1, T=65536,
+// C=5120), and a batch of two measured no faster.
+template <typename IO>
+constexpr int fold_batch() { return 1; }
 constexpr int kPollSleep = 2;  // s_sleep between polls (units of 64 clocks)
 
 struct TileRecs {
@@ -529,29 +543,13 @@ __device__ __forceinline__ bool should_stop(const FwdArgs& args, const TileRecs&
            __hip_atomic_load(&args.ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == R.give_up_word;
 }
 
-// Read the record of (chunk, slot) for this lane's channel, re-reading until every
-// word carries `tag`.  Returns false after giving up.
-__device__ __forceinline__ bool read_record(const FwdArgs& args, const TileRecs& R, int chunk, int slot,
-                                            uint32_t tag, int lane, Carry& out) {
-    for (uint32_t spin = 0;; ++spin) {
-        const uint64_t wa = ld_word(R.word(chunk, slot, 0, lane));
-        const uint64_t wb = ld_word(R.word(chunk, slot, 1, lane));
-        const uint64_t wp = ld_word(R.word(chunk, slot, 2, lane));
-        const bool good = word_tag(wa) == tag && word_tag(wb) == tag && word_tag(wp) == tag;
-        out = Carry{word_val(wa), word_val(wb), (double)word_val(wp)};
-        if (__all(good)) return true;
-        if (should_stop(args, R, spin)) return give_up(args, R, lane);
-        __builtin_amdgcn_s_sleep(kPollSleep);
-    }
-}
-
 // The state entering chunk ci (ci >= 1): lane l inspects the status of chunk ci-1-l,
 // 64 chunks per window, until the nearest inclusive record is found with every chunk
 // after it published; the state is then folded forward from that inclusive record
 // through the aggregates in chunk order with advance(), reproducing the canonical
 // chain bit for bit.  Gives up (raising the give-up word) after kMaxSpins polls, or
 // soon after another tile has given up, so every wave always finishes.
-template <int TILE>
+template <int TILE, int FB>
 __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan& ch, int ci,
                                           int lane, Carry& out) {
     int nearest = ci - 1;  // chunk inspected by lane 0 in the current window
@@ -584,19 +582,26 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
         if (!window_done) break;
         nearest -= 64;
     }
-    Carry P;
-    if (!read_record(args, R, start, 1, R.tag_incl, lane, P)) return false;
+    // fold forward from the inclusive record of `start` through the aggregates after it,
+    // FB aggregates per round; the first round also loads the inclusive record, and a
+    // round re-reads its words until every tag matches
     const double decay = (double)TILE * w2_of(ch);
-    // forward fold over the aggregates, kFoldBatch records per round; a round re-reads
-    // its batch until every word's tag matches
+    Carry P{0.f, 0.f, 0.0};
+    bool have_p = false;
 #pragma unroll 1
-    for (int c0 = start + 1; c0 < ci; c0 += kFoldBatch) {
-        const int n = min(kFoldBatch, ci - c0);
-        uint64_t t[kFoldBatch][3];
+    for (int c0 = start + 1;;) {
+        const int n = min(FB, ci - c0);
+        uint64_t inc[3], t[FB][3];
         for (uint32_t spin = 0;; ++spin) {
             bool good = true;
+            if (!have_p)
 #pragma unroll
-            for (int j = 0; j < kFoldBatch; ++j)
+                for (int q = 0; q < 3; ++q) {
+                    inc[q] = ld_word(R.word(start, 1, q, lane));
+                    good = good && word_tag(inc[q]) == R.tag_incl;
+                }
+#pragma unroll
+            for (int j = 0; j < FB; ++j)
                 if (j < n)
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
@@ -607,10 +612,15 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
             if (should_stop(args, R, spin)) return give_up(args, R, lane);
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
+        if (!have_p) {
+            P = Carry{word_val(inc[0]), word_val(inc[1]), (double)word_val(inc[2])};
+            have_p = true;
+        }
 #pragma unroll
-        for (int j = 0; j < kFoldBatch; ++j)
-            if (j < n)
-                P = advance(P, Carry{word_val(t[j][0]), word_val(t[j][1]), (double)word_val(t[j][2])}, decay);
+        for (int j = 0; j < FB; ++j)
+            if (j < n) P = advance(P, Carry{word_val(t[j][0]), word_val(t[j][1]), (double)word_val(t[j][2])}, decay);
+        c0 += n;
+        if (c0 >= ci) break;
     }
     out = P;
     return true;
@@ -678,7 +688,7 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
                                                       : empty_carry());
         } else {
             publish(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-            if (!look_back<TILE>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
+            if (!look_back<TILE, fold_batch<IO>()>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
         }
         const Carry incl = advance(prefix, agg_rec, (double)tile_len * w2_of(ch));
         if (ci + 1 < args.n_chunks) {

@@ -42,12 +42,13 @@ struct FwdArgs {
 };
 
 // How the chunked kernel moves k, v, y: float32 rows; bfloat16 rows at 2 bytes per lane;
-// bfloat16 row pairs at 4 bytes per lane (even C, 4-byte aligned k, v, y).
+// bfloat16 row pairs at 4 bytes per lane (even C, 4-byte aligned k, v, y).  Every mode
+// runs one channel per lane, 64 channels per group.
 enum IoMode { kIoF32 = 0, kIoBf16 = 1, kIoBf16Pair = 2 };
 
 // dtype: 0 = float32, 1 = bfloat16.
 hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s);
-// tile: 64, 128, 256 or 512 time steps per workgroup (one channel per lane, 64 per group).
+// tile: 64, 128, 256 or 512 time steps per workgroup.
 hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s);
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
