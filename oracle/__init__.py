@@ -11,6 +11,7 @@ It evaluates what the pages define, slowly and plainly:
 * ``wkv_recurrent``   -- the RNN-mode form with an (A, B) state, O(T)
 * ``wkv_step_ref``    -- one RNN-mode step from a given (a, b, p) state
 * ``wkv_mp``          -- the defining sums at 50 significant digits (mpmath)
+* ``wkv_backward_direct`` -- gradients of the defining sums, O(T^2)
 * ``scaled_error``    -- the scale-normalised error used as the parity gate
 
 Citations name the page ("Reinventing RNNs for the Transformer Era: RWKV",
@@ -27,3 +28,4 @@ from .wkv_oracle import (  # noqa: F401
     state_ratio,
 )
 from .wkv_mp import wkv_mp  # noqa: F401
+from .wkv_grad import wkv_backward_direct  # noqa: F401
