@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_device.h", "libwkv_api.cpp")
+KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_rows.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
 
 
 def kernel_source_hash() -> str:

@@ -160,6 +160,37 @@ wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                              wkv_algo algo, int64_t chunk_len, hipStream_t stream);
 
 /*
+ * Bytes of device workspace that wkv_backward needs for this problem (0 for
+ * empty problems, (size_t)-1 for invalid arguments).  About 0.47 bytes per
+ * element of k plus the forward chunked workspace at chunk length 128.
+ */
+size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt);
+
+/*
+ * Gradients of the whole-sequence WKV for the page's time-parallel training
+ * mode (section "Transformer-유사학습" trains through the WKV equation of
+ * section "WKV 연산자"): given gy = dL/dy for y = WKV(w, u, k, v) started from
+ * the empty state, writes
+ *   gk, gv : [B, T, C] device arrays of dtype dt, dL/dk and dL/dv;
+ *   gw, gu : [B, C] float32 device arrays, dL/dw and dL/du per lane (the
+ *            gradient of the shared [C] parameter is the sum over b).
+ * w, u, k, v are the forward inputs (the forward is recomputed; y is not
+ * needed), gy is [B, T, C] of dtype dt.  The outputs must not alias the
+ * inputs.  ws: device workspace of at least wkv_backward_workspace_bytes(...)
+ * bytes, zero-filled before its first use (wkv_forward_workspace_init fills
+ * any workspace) and owned by the library between calls; it starts with a
+ * forward control block, so wkv_forward_workspace_query reports on the
+ * forward scan inside the last call.  One workspace must not serve two calls
+ * that may run at the same time.  With T = 0, gw and gu are zero-filled.
+ * Deterministic: no atomics take part in any sum.
+ */
+wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                        const float* w, const float* u,
+                        const void* k, const void* v, const void* gy,
+                        void* gk, void* gv, float* gw, float* gu,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * One RNN-mode decoding step for N sequences x G layer slots x C channels
  * (section "RNN-유사추론" equation, and steps 4 and 7 of its decoding list:
  * update the WKV state, then store it for the next token).

@@ -137,6 +137,27 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     return wkv::launch_fwd_chunked(a, io, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
+// Workspace of the backward: the forward chunked workspace at kBwdTile (its control
+// block first, so the forward diagnostics read it too), then float32 planes of
+// [n_chunks][n_lanes]: 3 forward states entering each tile, 5 + 5 reverse aggregates
+// and carries, 2 partial sums.
+constexpr int kBwdPlanes = 3 + 5 + 5 + 2;
+
+struct BwdLayout {
+    ChunkLayout fwd;
+    size_t off_planes, plane_bytes, total;
+};
+
+BwdLayout backward_layout(int64_t B, int64_t T, int64_t C) {
+    BwdLayout L;
+    L.fwd = chunked_layout(B, T, C, wkv::kBwdTile);
+    const int64_t n_lanes = B * ceil_div(C, 64) * 64;
+    L.plane_bytes = align_up((size_t)ceil_div(T, wkv::kBwdTile) * (size_t)n_lanes * 4, kAlign);
+    L.off_planes = align_up(L.fwd.total, kAlign);
+    L.total = L.off_planes + kBwdPlanes * L.plane_bytes;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,6 +218,87 @@ wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt, cons
                              int64_t chunk_len, hipStream_t stream) {
     return forward_impl(B, T, C, dt, w, u, k, v, y, state_in_a, state_in_b, state_in_p, state_out_a,
                         state_out_b, state_out_p, ws, ws_bytes, algo, chunk_len, stream);
+}
+
+size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt) {
+    if (!sizes_ok(B, T, C) || !dtype_ok(dt)) return (size_t)-1;
+    if (B == 0 || T == 0 || C == 0) return 0;
+    return backward_layout(B, T, C).total;
+}
+
+wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                        const void* k, const void* v, const void* gy, void* gk, void* gv, float* gw,
+                        float* gu, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!sizes_ok(B, T, C)) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (B == 0 || C == 0) return WKV_OK;
+    if (!gw || !gu) return WKV_EINVAL;
+    if (T == 0) {  // no token: every gradient of w and u is zero
+        return wkv::launch_zero_words(gw, (size_t)(B * C), stream) == hipSuccess &&
+                       wkv::launch_zero_words(gu, (size_t)(B * C), stream) == hipSuccess
+                   ? WKV_OK
+                   : WKV_EHIP;
+    }
+    if (!w || !u || !k || !v || !gy || !gk || !gv) return WKV_EINVAL;
+    const BwdLayout L = backward_layout(B, T, C);
+    if (!ws || ws_bytes < L.total) return WKV_EWORKSPACE;
+    const int groups_per_row = (int)ceil_div(C, 64);
+    const int64_t n_groups = B * groups_per_row;
+    const int64_t n_chunks = ceil_div(T, wkv::kBwdTile);
+    if (n_groups * n_chunks > INT_MAX) return WKV_EINVAL;
+    // ws is at least 4-byte aligned by the caller's allocator; the layout aligns every part
+    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    float* planes = reinterpret_cast<float*>(base + L.off_planes);
+    const size_t ps = L.plane_bytes / 4;  // plane stride in floats (>= plane)
+
+    // 1. forward states entering every tile (no outputs)
+    wkv::FwdArgs f{};
+    f.w = w;
+    f.u = u;
+    f.k = k;
+    f.v = v;
+    f.y = nullptr;
+    f.B = (int)B;
+    f.T = (int)T;
+    f.C = (int)C;
+    f.groups_per_row = groups_per_row;
+    f.n_groups = (int)n_groups;
+    f.n_chunks = (int)n_chunks;
+    f.ctrl = reinterpret_cast<uint32_t*>(base);
+    f.status = reinterpret_cast<uint32_t*>(base + L.fwd.off_status);
+    f.recs = base + L.fwd.off_recs;
+    f.dump_a = planes;
+    f.dump_b = planes + ps;
+    f.dump_p = planes + 2 * ps;
+    if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), wkv::kBwdTile, stream) != hipSuccess)
+        return WKV_EHIP;
+
+    // 2-5. reverse scan and gradients
+    wkv::BwdArgs a{};
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.gy = gy;
+    a.gk = gk;
+    a.gv = gv;
+    a.gw = gw;
+    a.gu = gu;
+    a.fw_a = planes;
+    a.fw_b = planes + ps;
+    a.fw_p = planes + 2 * ps;
+    a.rv = planes + 3 * ps;
+    a.rin = planes + 8 * ps;
+    a.part = planes + 13 * ps;
+    a.plane = (long)ps;
+    a.B = (int)B;
+    a.T = (int)T;
+    a.C = (int)C;
+    a.groups_per_row = groups_per_row;
+    a.n_groups = (int)n_groups;
+    a.n_chunks = (int)n_chunks;
+    a.n_lanes = (long)(n_groups * 64);
+    return wkv::launch_bwd(a, dt == WKV_F32 ? 0 : 1, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

@@ -1,0 +1,442 @@
+// Backward of the WKV operator for gfx950: gradients of L = sum(gy * y) with respect to
+// k, v (per element) and w, u (per (b, c) lane).
+//
+// Page "Reinventing RNNs for the Transformer Era: RWKV" (velog review), section
+// "WKV 연산자" (WKV equation); the time-parallel training mode (section
+// "Transformer-유사학습") backpropagates through it.  With alpha_{t,i} the normalised
+// weight of token i in y_t, q_t = gy_t / D_t (D_t the WKV denominator) and the reverse
+// sums over the later outputs
+//   G_i = sum_{t>i} q_t e^{-(t-1-i) w},       H_i = sum_{t>i} q_t y_t e^{-(t-1-i) w},
+//   G'_i = sum_{t>i} (t-1-i) q_t e^{-(t-1-i) w},  H'_i likewise with q_t y_t,
+// the gradients are
+//   dL/dv_i = e^{k_i} G_i + e^{u+k_i} q_i
+//   dL/dk_i = e^{k_i} (v_i G_i - H_i) + e^{u+k_i} q_i (v_i - y_i)
+//   dL/du   = sum_i e^{u+k_i} q_i (v_i - y_i)
+//   dL/dw   = -sum_i e^{k_i} (v_i G'_i - H'_i)
+// and the sums obey G_{i-1} = q_i + e^{-w} G_i, H_{i-1} = q_i y_i + e^{-w} H_i,
+// G'_{i-1} = e^{-w} (G'_i + G_i), H'_{i-1} = e^{-w} (H'_i + H_i): a scan backwards in time.
+//
+// Plan (tiles of kBwdTile tokens x 64 channels, aligned with the forward tiles):
+//   1. the chunked forward kernel dumps the forward state entering every tile;
+//   2. bwd_tile_kernel<pass 0>: per tile, recompute y and q from that state and reduce
+//      the tile to its reverse aggregate (G, H, G', H' it contributes before its start);
+//   3. bwd_carry_kernel: per lane, a backwards scan over the tiles' aggregates gives the
+//      reverse carry entering every tile from the right;
+//   4. bwd_tile_kernel<pass 1>: per tile, recompute again and walk the tokens backwards
+//      from that carry, writing dL/dk, dL/dv and per-tile dL/dw, dL/du partials;
+//   5. bwd_reduce_kernel: per lane, sum the partials.
+// Every step is a deterministic function of its inputs (no atomics), so gradients are
+// bitwise reproducible.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wkv_device.h"
+#include "wkv_kernels.h"
+#include "wkv_rows.h"
+
+namespace wkv {
+
+// Reverse sums at one position: G = g 2^r, H = h 2^r, G' = gp 2^r, H' = hp 2^r
+// (r a float64 exponent in log2 units).
+struct Rev {
+    float g, h, gp, hp;
+    double r;
+};
+
+__device__ __forceinline__ Rev empty_rev() { return {0.f, 0.f, 0.f, 0.f, kEmptyP}; }
+
+// X (an earlier segment of n tokens, its sums at the position before it) followed by
+// the carry C (sums at X's last position from the tokens after X): the sums at the
+// position before X.  The later tokens are n steps further away, so C decays by
+// e^{-n w} and G' gains n G (each distance t-1-i grows by n).
+__device__ __forceinline__ Rev fold_rev(const Rev& x, const Rev& c, int n, double w2) {
+    const double rc = c.r - (double)n * w2;
+    const double rm = fmax(x.r, rc);
+    const float fx = ex2((float)(x.r - rm));
+    const float fc = ex2((float)(rc - rm));
+    const float nf = (float)n;
+    return {fmaf(x.g, fx, c.g * fc), fmaf(x.h, fx, c.h * fc), fmaf(x.gp, fx, fmaf(nf, c.g, c.gp) * fc),
+            fmaf(x.hp, fx, fmaf(nf, c.h, c.hp) * fc), rm};
+}
+
+// Same sums with the largest magnitude scaled into [0.5, 1) by an exact power of two.
+__device__ __forceinline__ Rev normalize_rev(const Rev& c) {
+    const float m = fmaxf(fmaxf(fabsf(c.g), fabsf(c.h)), fmaxf(fabsf(c.gp), fabsf(c.hp)));
+    if (m == 0.f) return empty_rev();
+    if (!(m < 3.0e38f)) return c;  // Inf and NaN pass through
+    int e;
+    (void)__builtin_frexpf(m, &e);
+    return {__builtin_ldexpf(c.g, -e), __builtin_ldexpf(c.h, -e), __builtin_ldexpf(c.gp, -e),
+            __builtin_ldexpf(c.hp, -e), c.r + (double)e};
+}
+
+// float32 storage form: reference rounded to float32, the exact residual folded in.
+__device__ __forceinline__ void store_rev(float* base, size_t plane, size_t i, const Rev& c) {
+    const float rf = fmaxf((float)c.r, -3.0e38f);
+    const float f = ex2((float)(c.r - (double)rf));
+    base[i] = c.g * f;
+    base[plane + i] = c.h * f;
+    base[2 * plane + i] = c.gp * f;
+    base[3 * plane + i] = c.hp * f;
+    base[4 * plane + i] = rf;
+}
+__device__ __forceinline__ Rev load_rev(const float* base, size_t plane, size_t i) {
+    return {base[i], base[plane + i], base[2 * plane + i], base[3 * plane + i], (double)base[4 * plane + i]};
+}
+
+// Fast path of one wave's L tokens in the frame of reference R (log2 units): x_j =
+// 2^(k_j log2e - R), q^_j = gy_j / (D_j 2^-R), so that every product e^{k_i} q_t of the
+// gradients is x_i q^_t.  After forward(): k holds x, g holds q^, y holds y.
+template <int L>
+struct BwdChunk {
+    float k[L], v[L], g[L], y[L];
+
+    template <typename IO>
+    __device__ __forceinline__ void load(const WaveRows& w, Rsrc gy, int nv, bool valid) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            k[j] = 0.f;
+            v[j] = 0.f;
+            g[j] = 0.f;
+            if (j < nv && valid) {
+                const uint32_t so = (uint32_t)j * w.row_bytes;
+                k[j] = load_elt<IO>(w.k, w.lane_off, so);
+                v[j] = load_elt<IO>(w.v, w.lane_off, so);
+                g[j] = load_elt<IO>(gy, w.lane_off, so);
+            }
+        }
+    }
+    __device__ __forceinline__ void range(float& kmax, float& kmin) const {
+        kmax = k[0];
+        kmin = k[0];
+#pragma unroll
+        for (int j = 1; j < L; ++j) {
+            kmax = fmaxf(kmax, k[j]);
+            kmin = fminf(kmin, k[j]);
+        }
+    }
+    // forward state of the wave's tokens from the empty state (frame R); k becomes x
+    __device__ __forceinline__ Carry aggregate(const Chan& ch, float R) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            k[j] = ex2(fmaf(k[j], kLog2e, -R));
+            a = fmaf(ch.d, a, k[j] * v[j]);
+            b = fmaf(ch.d, b, k[j]);
+        }
+        return Carry{a, b, (double)R};
+    }
+    // y and q^ from the forward state entering the wave (normalised, p - R <= kSpan)
+    __device__ __forceinline__ void forward(const Chan& ch, const Carry& cin, float R) {
+        const float s = ex2((float)(cin.p - (double)R));
+        float a = cin.a * s, b = cin.b * s;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const float x = k[j];
+            const float xv = x * v[j];
+            const float inv = rcp(fmaf(ch.eu, x, b));
+            y[j] = fmaf(ch.eu, xv, a) * inv;
+            g[j] = g[j] * inv;
+            a = fmaf(ch.d, a, xv);
+            b = fmaf(ch.d, b, x);
+        }
+    }
+    // reverse sums at the position before the wave from its own tokens (frame R)
+    __device__ __forceinline__ Rev reverse_aggregate(const Chan& ch, float R) const {
+        float G = 0.f, H = 0.f, Gp = 0.f, Hp = 0.f;
+#pragma unroll
+        for (int j = L - 1; j >= 0; --j) {
+            Gp = ch.d * (Gp + G);
+            Hp = ch.d * (Hp + H);
+            G = fmaf(ch.d, G, g[j]);
+            H = fmaf(ch.d, H, g[j] * y[j]);
+        }
+        return Rev{G, H, Gp, Hp, -(double)R};
+    }
+    // gradients from the reverse carry at the wave's last position; k, v are replaced
+    // by dL/dk, dL/dv; accumulates the lane's dL/dw, dL/du
+    __device__ __forceinline__ void backward(const Chan& ch, const Rev& cin, float R, float& gw, float& gu) {
+        const float s = ex2((float)(cin.r + (double)R));
+        float G = cin.g * s, H = cin.h * s, Gp = cin.gp * s, Hp = cin.hp * s;
+#pragma unroll
+        for (int j = L - 1; j >= 0; --j) {
+            const float x = k[j], vj = v[j], qj = g[j], yj = y[j];
+            const float cur = ch.eu * x * qj;  // e^{u+k_j} q_j
+            const float dvy = vj - yj;
+            v[j] = fmaf(x, G, cur);                   // dL/dv_j
+            k[j] = fmaf(x, fmaf(vj, G, -H), cur * dvy);  // dL/dk_j
+            gw = fmaf(-x, fmaf(vj, Gp, -Hp), gw);
+            gu = fmaf(cur, dvy, gu);
+            Gp = ch.d * (Gp + G);
+            Hp = ch.d * (Hp + H);
+            G = fmaf(ch.d, G, qj);
+            H = fmaf(ch.d, H, qj * yj);
+        }
+    }
+};
+
+// Exact path for one wave (any input): per token, the forward state is recomputed from
+// the state entering the wave by walking the earlier tokens of the wave again (O(L^2),
+// read from memory, no per-token arrays), and the reverse sums carry their own float64
+// exponent.  Produces the wave's reverse aggregate (pass 0) or its gradients (pass 1).
+template <typename IO, bool OUT>
+__device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, const Rev& rin, const WaveRows& w,
+                                          Rsrc gyr, Rsrc gkr, Rsrc gvr, int nv, bool valid, float& gw, float& gu) {
+    Rev c = rin;
+    const double w2 = w2_of(ch), u2 = u2_of(ch);
+#pragma unroll 1
+    for (int j = nv - 1; j >= 0; --j) {
+        // forward state entering token j
+        Carry st = fin;
+#pragma unroll 1
+        for (int i = 0; i < j; ++i) {
+            const uint32_t so = (uint32_t)i * w.row_bytes;
+            const float ki = valid ? load_elt<IO>(w.k, w.lane_off, so) : 0.f;
+            const float vi = valid ? load_elt<IO>(w.v, w.lane_off, so) : 0.f;
+            (void)lse_token<false>(ch, st, ki, vi);
+        }
+        const uint32_t so = (uint32_t)j * w.row_bytes;
+        const float kj = valid ? load_elt<IO>(w.k, w.lane_off, so) : 0.f;
+        const float vj = valid ? load_elt<IO>(w.v, w.lane_off, so) : 0.f;
+        const float gj = valid ? load_elt<IO>(gyr, w.lane_off, so) : 0.f;
+        // y_j and q_j = gy_j / D_j = qm 2^qe
+        const double k2 = (double)kj * kLog2eD;
+        const double uk = u2 + k2;
+        const double qref = fmax(st.p, uk);
+        const float e1 = ex2((float)(st.p - qref));
+        const float e2 = ex2((float)(uk - qref));
+        const float inv = rcp(fmaf(e1, st.b, e2));
+        const float yj = fmaf(e1, st.a, e2 * vj) * inv;
+        const float qm = gj * inv;
+        const double qe = -qref;
+        if (OUT) {
+            const float ek = ex2((float)(k2 + c.r));         // e^{k_j} 2^r
+            const float cur = ex2((float)(uk + qe)) * qm;   // e^{u+k_j} q_j
+            const float dvy = vj - yj;
+            const float dv = fmaf(ek, c.g, cur);
+            const float dk = fmaf(ek, fmaf(vj, c.g, -c.h), cur * dvy);
+            gw = fmaf(-ek, fmaf(vj, c.gp, -c.hp), gw);
+            gu = fmaf(cur, dvy, gu);
+            if (valid) {
+                store_elt<IO>(gkr, w.lane_off, so, dk);
+                store_elt<IO>(gvr, w.lane_off, so, dv);
+            }
+        }
+        // reverse sums at the position before token j
+        const double rd = c.r - w2;
+        const double rn = fmax(rd, qe);
+        const float f1 = ex2((float)(rd - rn));
+        const float f2 = ex2((float)(qe - rn));
+        c = normalize_rev(Rev{fmaf(f2, qm, f1 * c.g), fmaf(f2, qm * yj, f1 * c.h), f1 * (c.gp + c.g),
+                              f1 * (c.hp + c.h), rn});
+    }
+    return c;
+}
+
+// Everything a tile's waves share.
+template <int NW>
+struct BwdShared {
+    float a[NW][64];  // forward: per-wave aggregate, then the state before each wave
+    float b[NW][64];
+    double p[NW][64];
+    float g[NW][64];  // reverse: per-wave aggregate, then the carry after each wave
+    float h[NW][64];
+    float gp[NW][64];
+    float hp[NW][64];
+    double r[NW][64];
+    float gw[NW][64];  // per-wave partial sums
+    float gu[NW][64];
+};
+
+// Fast-path bound for the reverse carry in a wave's frame: G^ = g 2^(r + R) with |g| < 1.
+constexpr float kSpanRev = 60.f;
+
+template <typename IO, int L, int NW, int PASS>
+__global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
+    constexpr int TILE = L * NW;
+    static_assert(TILE == kBwdTile, "tiles must line up with the dumped forward tiles");
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int C = args.C, T = args.T;
+    __shared__ BwdShared<NW> sh;
+
+    const int g = blockIdx.x % args.n_groups;
+    const int ci = blockIdx.x / args.n_groups;
+    const int bi = g / args.groups_per_row;
+    const int c_grp = (g - bi * args.groups_per_row) * 64;
+    const int c = c_grp + lane;
+    const bool cvalid = c < C;
+    const int t_tile = ci * TILE;
+    const int t0 = __builtin_amdgcn_readfirstlane(t_tile + wid * L);
+    const int nv = max(0, min(L, T - t0));
+    const size_t li = (size_t)g * 64 + lane;                  // lane index
+    const size_t ti = (size_t)ci * args.n_lanes + li;         // (tile, lane) index
+    const size_t plane = (size_t)args.plane;
+
+    WaveRows rows;
+    const size_t off = (((size_t)bi * T + (size_t)min(t0, T)) * C + c_grp) * sizeof(IO);
+    rows.k = make_rsrc(static_cast<const char*>(args.k) + off);
+    rows.v = make_rsrc(static_cast<const char*>(args.v) + off);
+    rows.y = make_rsrc(static_cast<char*>(args.gk) + off);  // unused by the row helpers here
+    rows.lane_off = (uint32_t)(lane * sizeof(IO));
+    rows.row_bytes = (uint32_t)(C * sizeof(IO));
+    const Rsrc gyr = make_rsrc(static_cast<const char*>(args.gy) + off);
+    const Rsrc gkr = make_rsrc(static_cast<char*>(args.gk) + off);
+    const Rsrc gvr = make_rsrc(static_cast<char*>(args.gv) + off);
+
+    BwdChunk<L> ck;
+    ck.template load<IO>(rows, gyr, nv, cvalid);
+
+    const Chan ch = make_chan(args.w[cvalid ? c : 0], args.u[cvalid ? c : 0]);
+    const double w2 = w2_of(ch);
+    float kmax, kmin;
+    ck.range(kmax, kmin);
+    const float R = kmax * kLog2e;
+    const bool fast = __all(nv == L && chunk_fast_ok(ch, kmax, kmin));
+
+    // ---- forward: per-wave aggregate, combined into the state before each wave ----
+    Carry agg = empty_carry();
+    if (fast) {
+        agg = ck.aggregate(ch, R);
+    } else {
+        lse_walk<IO, false>(ch, agg, rows, nv, cvalid, false);
+    }
+    sh.a[wid][lane] = agg.a;
+    sh.b[wid][lane] = agg.b;
+    sh.p[wid][lane] = agg.p;
+    __syncthreads();
+    if (wid == 0) {
+        Carry run = normalize(Carry{args.fw_a[ti], args.fw_b[ti], (double)args.fw_p[ti]});
+#pragma unroll 1
+        for (int wv = 0; wv < NW; ++wv) {
+            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
+            const Carry aw{sh.a[wv][lane], sh.b[wv][lane], sh.p[wv][lane]};
+            sh.a[wv][lane] = run.a;
+            sh.b[wv][lane] = run.b;
+            sh.p[wv][lane] = run.p;
+            run = normalize(combine(run, aw, (double)nvw * w2));
+        }
+    }
+    __syncthreads();
+    const Carry fin = normalize(Carry{sh.a[wid][lane], sh.b[wid][lane], sh.p[wid][lane]});
+
+    // ---- per-wave reverse aggregate (from nothing after the wave) ----
+    const bool wave_fast = fast && __all(fin.p - (double)R <= (double)kSpan);
+    float gw = 0.f, gu = 0.f;
+    Rev ragg;
+    if (wave_fast) {
+        ck.forward(ch, fin, R);
+        ragg = ck.reverse_aggregate(ch, R);
+    } else {
+        ragg = exact_wave<IO, false>(ch, fin, empty_rev(), rows, gyr, gkr, gvr, nv, cvalid, gw, gu);
+    }
+    ragg = normalize_rev(ragg);
+    sh.g[wid][lane] = ragg.g;
+    sh.h[wid][lane] = ragg.h;
+    sh.gp[wid][lane] = ragg.gp;
+    sh.hp[wid][lane] = ragg.hp;
+    sh.r[wid][lane] = ragg.r;
+    __syncthreads();
+
+    // ---- combine backwards: the carry after each wave (pass 1) or the tile aggregate ----
+    if (wid == 0) {
+        Rev run = PASS == 0 ? empty_rev() : normalize_rev(load_rev(args.rin, plane, ti));
+#pragma unroll 1
+        for (int wv = NW - 1; wv >= 0; --wv) {
+            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
+            const Rev rw{sh.g[wv][lane], sh.h[wv][lane], sh.gp[wv][lane], sh.hp[wv][lane], sh.r[wv][lane]};
+            sh.g[wv][lane] = run.g;  // slot wv now holds the carry after wave wv
+            sh.h[wv][lane] = run.h;
+            sh.gp[wv][lane] = run.gp;
+            sh.hp[wv][lane] = run.hp;
+            sh.r[wv][lane] = run.r;
+            run = normalize_rev(fold_rev(rw, run, nvw, w2));
+        }
+        if (PASS == 0) store_rev(args.rv, plane, ti, run);
+    }
+    if (PASS == 0) return;
+    __syncthreads();
+
+    // ---- pass 1: gradients of this wave's tokens from the carry after the wave ----
+    const Rev cin{sh.g[wid][lane], sh.h[wid][lane], sh.gp[wid][lane], sh.hp[wid][lane], sh.r[wid][lane]};
+    if (wave_fast && __all(cin.r + (double)R <= (double)kSpanRev)) {
+        ck.backward(ch, cin, R, gw, gu);
+        if (cvalid) {
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                store_elt<IO>(gkr, rows.lane_off, (uint32_t)j * rows.row_bytes, ck.k[j]);
+                store_elt<IO>(gvr, rows.lane_off, (uint32_t)j * rows.row_bytes, ck.v[j]);
+            }
+        }
+    } else {
+        gw = 0.f;
+        gu = 0.f;
+        (void)exact_wave<IO, true>(ch, fin, cin, rows, gyr, gkr, gvr, nv, cvalid, gw, gu);
+    }
+    sh.gw[wid][lane] = gw;
+    sh.gu[wid][lane] = gu;
+    __syncthreads();
+    if (wid == 0) {
+        float sw = 0.f, su = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            sw += sh.gw[wv][lane];
+            su += sh.gu[wv][lane];
+        }
+        args.part[ti] = sw;
+        args.part[plane + ti] = su;
+    }
+}
+
+// Per lane, backwards over the tiles: the carry entering each tile from the right.
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs args) {
+    const long li = (long)blockIdx.x * 256 + threadIdx.x;
+    if (li >= args.n_lanes) return;
+    const int g = (int)(li / 64);
+    const int c = (g % args.groups_per_row) * 64 + (int)(li % 64);
+    const double w2 = (double)args.w[c < args.C ? c : 0] * kLog2eD;
+    const size_t plane = (size_t)args.plane;
+    Rev run = empty_rev();
+    for (int ci = args.n_chunks - 1; ci >= 0; --ci) {
+        const size_t ti = (size_t)ci * args.n_lanes + li;
+        store_rev(args.rin, plane, ti, run);
+        const int n = min(kBwdTile, args.T - ci * kBwdTile);
+        run = normalize_rev(fold_rev(normalize_rev(load_rev(args.rv, plane, ti)), run, n, w2));
+    }
+}
+
+// Per lane: dL/dw and dL/du as the sums of the tiles' partials.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs args) {
+    const long li = (long)blockIdx.x * 256 + threadIdx.x;
+    if (li >= args.n_lanes) return;
+    const int g = (int)(li / 64);
+    const int bi = g / args.groups_per_row;
+    const int c = (g % args.groups_per_row) * 64 + (int)(li % 64);
+    if (c >= args.C) return;
+    const size_t plane = (size_t)args.plane;
+    float sw = 0.f, su = 0.f;
+    for (int ci = 0; ci < args.n_chunks; ++ci) {
+        sw += args.part[(size_t)ci * args.n_lanes + li];
+        su += args.part[plane + (size_t)ci * args.n_lanes + li];
+    }
+    args.gw[(size_t)bi * args.C + c] = sw;
+    args.gu[(size_t)bi * args.C + c] = su;
+}
+
+template <typename IO>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+    constexpr int L = 16, NW = kBwdTile / L;
+    const unsigned tiles = (unsigned)((long)a.n_groups * a.n_chunks);
+    const unsigned lane_blocks = (unsigned)((a.n_lanes + 255) / 256);
+    hipLaunchKernelGGL((bwd_tile_kernel<IO, L, NW, 0>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL(bwd_carry_kernel, dim3(lane_blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_tile_kernel<IO, L, NW, 1>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(lane_blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_bwd_t<float>(a, s) : launch_bwd_t<uint16_t>(a, s);
+}
+
+}  // namespace wkv

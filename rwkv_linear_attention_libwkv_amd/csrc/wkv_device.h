@@ -85,6 +85,13 @@ __device__ __forceinline__ bool chan_fast_ok(const Chan& c) {
     return (c.w >= 0.f) && (c.w <= 3.0e38f) && (u2 <= kSpan) && (u2 >= -kSpan);
 }
 
+// Fast-path conditions of a chunk: channel constants, the key range and the bonus stay
+// within kSpan of the reference R = max k (log2 units).
+__device__ __forceinline__ bool chunk_fast_ok(const Chan& ch, float kmax, float kmin) {
+    const float range = (kmax - kmin) * kLog2e;
+    return chan_fast_ok(ch) && (range <= kSpan) && (range - ch.u * kLog2e <= kSpan);
+}
+
 // float32 -> float32 state triple of the ABI (natural-log p) from a Carry.
 __device__ __forceinline__ void carry_to_abi(const Carry& c, float& a, float& b, float& p) {
     if (c.b == 0.f && c.a == 0.f) {  // empty

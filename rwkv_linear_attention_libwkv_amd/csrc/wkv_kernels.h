@@ -33,6 +33,9 @@ struct FwdArgs {
     float* sout_p;
     // chunked algorithm only (workspace carve-up)
     uint32_t* ctrl;  // control block, kCtrlWords words
+    float* dump_a;     // optional [n_chunks][n_groups * 64] state entering each tile (record
+    float* dump_b;     //   form: A = a 2^p, B = b 2^p, p in log2 units); with y null the
+    float* dump_p;     //   kernel writes only these (no outputs)
     uint32_t* status;  // [n_groups][n_chunks] status hints
     void* recs;        // [n_chunks][n_groups][2][3][64] tagged 64-bit words
     int B, T, C;
@@ -53,6 +56,32 @@ hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s)
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
                              float* ob, float* op, long n, hipStream_t s);
+
+// Backward of the chunked forward (gradients of sum(gy * y)), in tiles of kBwdTile tokens
+// x 64 channels that line up with the forward tiles whose entering states were dumped.
+constexpr int kBwdTile = 128;
+struct BwdArgs {
+    const float* w;
+    const float* u;
+    const void* k;   // [B, T, C] dtype
+    const void* v;
+    const void* gy;  // dL/dy
+    void* gk;        // [B, T, C] dtype, written by pass 1
+    void* gv;
+    float* gw;       // [B, C] per-lane dL/dw, written by the reduction
+    float* gu;
+    const float* fw_a;  // [n_chunks][n_lanes] forward state entering each tile (dump)
+    const float* fw_b;
+    const float* fw_p;
+    float* rv;       // [5][n_chunks][n_lanes] reverse aggregate of each tile (pass 0)
+    float* rin;      // [5][n_chunks][n_lanes] reverse carry entering each tile from the right
+    float* part;     // [2][n_chunks][n_lanes] per-tile dL/dw, dL/du partial sums
+    long plane;      // float stride between the planes of fw_*, rv, rin, part (>= n_chunks * n_lanes)
+    int B, T, C;
+    int groups_per_row, n_groups, n_chunks;
+    long n_lanes;    // n_groups * 64
+};
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t s);
 
 struct StepArgs {
     const float* w;  // [G, C]

@@ -29,6 +29,8 @@ EXPORTS = (
     "wkv_forward_ex",
     "wkv_forward_state",
     "wkv_step",
+    "wkv_backward_workspace_bytes",
+    "wkv_backward",
     "wkv_status_string",
 )
 
@@ -65,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.wkv_forward_state.restype = i32
     lib.wkv_step.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.wkv_step.restype = i32
+    lib.wkv_backward_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.wkv_backward_workspace_bytes.restype = sz
+    lib.wkv_backward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.wkv_backward.restype = i32
     lib.wkv_status_string.argtypes = [i32]
     lib.wkv_status_string.restype = ctypes.c_char_p
     return lib
@@ -207,6 +213,53 @@ def wkv_step(w, u, k, v, a, b, p, *, y=None, stream=None):
     return y
 
 
+def wkv_backward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32) -> int:
+    n = lib.wkv_backward_workspace_bytes(B, T, C, _dtype_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid arguments for the workspace query")
+    return int(n)
+
+
+def new_backward_workspace(B: int, T: int, C: int, dtype=torch.float32, device="cuda"):
+    """A ready (zero-filled) backward workspace for these sizes, or None if none is needed."""
+    need = wkv_backward_workspace_bytes(B, T, C, dtype)
+    if not need:
+        return None
+    ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
+    return wkv_forward_workspace_init(ws)
+
+
+def wkv_backward(w, u, k, v, gy, *, gk=None, gv=None, gw=None, gu=None, workspace=None, stream=None):
+    """Gradients of sum(gy * WKV(w, u, k, v)): returns (gw, gu, gk, gv).
+
+    k, v, gy: [B, T, C] (float32 or bfloat16, on the GPU); gk, gv have their dtype;
+    gw, gu are float32 [B, C] per-lane gradients (sum over B for the [C] parameters).
+    """
+    _need(k.dim() == 3 and v.shape == k.shape and gy.shape == k.shape, "k, v and gy must be [B, T, C]")
+    _need(k.is_cuda and v.is_cuda and gy.is_cuda and w.is_cuda and u.is_cuda, "all tensors must be on the GPU")
+    _need(k.dtype == v.dtype == gy.dtype, "k, v and gy must share a dtype")
+    _need(k.is_contiguous() and v.is_contiguous() and gy.is_contiguous(), "k, v and gy must be contiguous")
+    B, T, C = k.shape
+    _need(w.dtype == torch.float32 and u.dtype == torch.float32, "w and u must be float32")
+    _need(w.numel() == C and u.numel() == C and w.is_contiguous() and u.is_contiguous(),
+          "w and u must be contiguous with C entries")
+    gk = torch.empty_like(k) if gk is None else gk
+    gv = torch.empty_like(k) if gv is None else gv
+    for t in (gk, gv):
+        _need(t.shape == k.shape and t.dtype == k.dtype and t.is_contiguous(), "bad gk or gv")
+    gw = torch.empty((B, C), dtype=torch.float32, device=k.device) if gw is None else gw
+    gu = torch.empty((B, C), dtype=torch.float32, device=k.device) if gu is None else gu
+    for t in (gw, gu):
+        _need(t.numel() == B * C and t.dtype == torch.float32 and t.is_contiguous(), "bad gw or gu")
+    if workspace is None:
+        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wkv_backward(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                            _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(workspace), ws_bytes, _stream(stream)),
+           "wkv_backward")
+    return gw, gu, gk, gv
+
+
 def empty_state(shape, device="cuda"):
     """(a, b, p) float32 tensors of the empty state (a = b = 0, p = P_EMPTY)."""
     a = torch.zeros(shape, dtype=torch.float32, device=device)
@@ -237,4 +290,5 @@ def workspace_epoch(workspace, stream=None) -> int:
 # short aliases
 forward = wkv_forward
 step = wkv_step
+backward = wkv_backward
 workspace_bytes = wkv_forward_workspace_bytes

@@ -130,6 +130,19 @@ def forward_inputs(spec: ForwardSpec) -> dict:
     return {"w": w, "u": u, "k": k, "v": v, "dtype": spec.dtype}
 
 
+def backward_inputs(spec: ForwardSpec) -> dict:
+    """forward_inputs(spec) plus gy = dL/dy ~ N(0, 1) of shape [B, T, C].
+
+    gy comes from its own stream, ``default_rng(seed + 7_777_777)``, so the forward
+    inputs are those of the forward workload; bf16 workloads round it like k and v.
+    """
+    inp = forward_inputs(spec)
+    rng = np.random.default_rng(spec.seed + 7_777_777)
+    gy = rng.standard_normal(size=(spec.B, spec.T, spec.C), dtype=np.float32)
+    inp["gy"] = round_to_bf16(gy) if spec.dtype == "bf16" else gy
+    return inp
+
+
 def step_params(spec: StepSpec) -> tuple:
     """(w, u) of a decode workload, shape [G, C], float32."""
     rng = np.random.default_rng(spec.seed)

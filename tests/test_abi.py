@@ -121,6 +121,45 @@ def test_step_argument_checks():
         assert step(1, 2, 2, ptrs=tuple(ptrs)) == EINVAL, i
 
 
+def test_backward_argument_checks():
+    def bwd(B, T, C, dt=F32, ptrs=(P,) * 9, ws=NULL, ws_bytes=0):
+        return lib.wkv_backward(B, T, C, dt, *ptrs, ws, ws_bytes, None)
+    assert bwd(-1, 4, 4) == EINVAL
+    assert bwd(1, -4, 4) == EINVAL
+    assert bwd(1, 1 << 31, 4) == EINVAL
+    assert bwd(1, 4, 4, dt=5) == EDTYPE
+    assert bwd(0, 4, 4, ptrs=(NULL,) * 9) == OK
+    assert bwd(4, 4, 0, ptrs=(NULL,) * 9) == OK
+    # every pointer operand is required for a non-empty problem (gw, gu even with T = 0)
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = NULL
+        assert bwd(2, 300, 64, ptrs=tuple(ptrs), ws=P, ws_bytes=1 << 30) == EINVAL, i
+    for i in (7, 8):
+        ptrs = [P] * 9
+        ptrs[i] = NULL
+        assert bwd(2, 0, 64, ptrs=tuple(ptrs)) == EINVAL, i
+    need = lib.wkv_backward_workspace_bytes(2, 300, 64, F32)
+    assert need > 0
+    assert bwd(2, 300, 64) == EWS
+    assert bwd(2, 300, 64, ws=P, ws_bytes=need - 1) == EWS
+
+
+def test_backward_workspace_query():
+    q = lib.wkv_backward_workspace_bytes
+    bad = ctypes.c_size_t(-1).value
+    assert q(-1, 4, 4, F32) == bad
+    assert q(1, 4, 4, 9) == bad
+    assert q(0, 4, 4, F32) == 0 and q(4, 0, 4, F32) == 0
+    a = q(8, 8192, 2048, F32)
+    assert a == q(8, 8192, 2048, BF16)
+    # about 0.47 bytes per element plus the forward records (0.375 per element at 128)
+    elems = 8 * 8192 * 2048
+    assert 0.8 * elems < a < 0.9 * elems + (1 << 20)
+    # it holds a forward chunked workspace at chunk length 128
+    assert a > lib.wkv_forward_workspace_bytes(8, 8192, 2048, F32, 2, 128)
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import importlib
 
