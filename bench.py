@@ -9,8 +9,9 @@ with inputs resident in HBM, bracketed by torch.cuda.synchronize().  Prints one
 JSON line: elements/s (B*T*C per second), the HBM roofline of the forward kernel
 (algorithmic bytes: read k, v, write y) measured with HIP events on the launch
 stream, and the float64 CPU oracle timed on the host as a reported baseline.
-The other workloads (169M width, 64K-token bf16, batched decode step) are timed
-the same way and reported under "other_workloads".
+The other workloads (169M width, 64K-token bf16, the backward at the 8K-context
+and 64K-token shapes, batched decode step) are timed the same way and reported
+under "other_workloads".
 """
 from __future__ import annotations
 
@@ -26,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_rows.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
+KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_backward.hip", "wkv_rows.h", "wkv_device.h",
+                  "wkv_kernels.h", "libwkv_api.cpp")
 
 
 def kernel_source_hash() -> str:
@@ -119,6 +121,48 @@ def forward_case(spec, steps, warmup, gen="numpy"):
     return out
 
 
+def backward_case(spec, steps, warmup):
+    """wkv_backward over a forward workload's shape with gy ~ N(0, 1) drawn on the device."""
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(spec.seed)
+    w_np, u_np = workloads.channel_params(rng, (spec.C,), spec.w_raw_lo, spec.w_raw_hi, spec.u_std)
+    w, u = torch.from_numpy(w_np).cuda(), torch.from_numpy(u_np).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(spec.seed)
+    shape = (spec.B, spec.T, spec.C)
+    k = (torch.randn(shape, generator=g, device="cuda") * spec.k_std).to(dt)
+    v = (torch.randn(shape, generator=g, device="cuda") * spec.v_std).to(dt)
+    gy = torch.randn(shape, generator=g, device="cuda").to(dt)
+    gk, gv = torch.empty_like(k), torch.empty_like(k)
+    gw = torch.empty((spec.B, spec.C), device="cuda")
+    gu = torch.empty_like(gw)
+    ws = libwkv.new_backward_workspace(spec.B, spec.T, spec.C, dt)
+
+    def fn():
+        libwkv.wkv_backward(w, u, k, v, gy, gk=gk, gv=gv, gw=gw, gu=gu, workspace=ws)
+
+    wall, per_call = time_launches(fn, steps, warmup)
+    assert libwkv.lookback_error(ws) == 0, "look-back gave up"
+    elt = 4 if spec.dtype == "f32" else 2
+    bytes_per_launch = 5 * elt * spec.elements + 8 * spec.B * spec.C  # read k, v, gy; write gk, gv, gw, gu
+    out = {
+        "workload": spec.name.replace("wkv_fwd", "wkv_bwd"),
+        "elements": spec.elements,
+        "per_launch_s": per_call,
+        "elements_per_s": spec.elements / per_call,
+        "algorithmic_bytes_per_launch": bytes_per_launch,
+        "achieved_GBps": bytes_per_launch / per_call / 1e9,
+    }
+    del k, v, gy, gk, gv, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def step_case(spec, steps, warmup):
     import torch
 
@@ -196,6 +240,10 @@ def profile_run(name, launches):
         spec = workloads.FORWARD_SPECS[name]
         r = forward_case(spec, launches, 1, gen="torch")
         print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch", flush=True)
+    elif name.replace("wkv_bwd", "wkv_fwd") in workloads.FORWARD_SPECS:
+        spec = workloads.FORWARD_SPECS[name.replace("wkv_bwd", "wkv_fwd")]
+        r = backward_case(spec, launches, 1)
+        print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/call", flush=True)
     else:
         r = step_case(workloads.STEP_DECODE, 4, 1)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step", flush=True)
@@ -247,6 +295,11 @@ def main():
             others.append(r)
             print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch, {r['achieved_GBps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
+        for s in (workloads.FWD_CTX8K, workloads.FWD_LONG_BF16):
+            r = backward_case(s, max(5, args.steps // 2), 2)
+            others.append(r)
+            print(f"# {r['workload']}: {r['per_launch_s'] * 1e6:.1f} us/call, {r['achieved_GBps']:.0f} GB/s "
+                  f"(algorithmic bytes)", file=sys.stderr, flush=True)
         r = step_case(workloads.STEP_DECODE, args.steps, 1)
         others.append(r)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "

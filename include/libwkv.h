@@ -161,8 +161,9 @@ wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
 
 /*
  * Bytes of device workspace that wkv_backward needs for this problem (0 for
- * empty problems, (size_t)-1 for invalid arguments).  About 0.47 bytes per
- * element of k plus the forward chunked workspace at chunk length 128.
+ * empty problems, (size_t)-1 for invalid arguments): about 1.16 bytes per
+ * element of k (the records of the forward and backward scans over tiles of
+ * 128 time steps, and five float32 values per tile and channel).
  */
 size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt);
 
@@ -178,11 +179,13 @@ size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype d
  * needed), gy is [B, T, C] of dtype dt.  The outputs must not alias the
  * inputs.  ws: device workspace of at least wkv_backward_workspace_bytes(...)
  * bytes, zero-filled before its first use (wkv_forward_workspace_init fills
- * any workspace) and owned by the library between calls; it starts with a
- * forward control block, so wkv_forward_workspace_query reports on the
- * forward scan inside the last call.  One workspace must not serve two calls
- * that may run at the same time.  With T = 0, gw and gu are zero-filled.
- * Deterministic: no atomics take part in any sum.
+ * any workspace) and owned by the library between calls; it starts with the
+ * same control block as a forward workspace, so wkv_forward_workspace_query
+ * reports on the last call (gave_up if either of its two scans, forward then
+ * backward in time, gave up; each call advances the epoch by two).  One
+ * workspace must not serve two calls that may run at the same time.  With
+ * T = 0, gw and gu are zero-filled.  Deterministic: no atomics take part in
+ * any sum.
  */
 wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                         const float* w, const float* u,

@@ -138,22 +138,26 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
 }
 
 // Workspace of the backward: the forward chunked workspace at kBwdTile (its control
-// block first, so the forward diagnostics read it too), then float32 planes of
-// [n_chunks][n_lanes]: 3 forward states entering each tile, 5 + 5 reverse aggregates
-// and carries, 2 partial sums.
-constexpr int kBwdPlanes = 3 + 5 + 5 + 2;
+// block first, so the forward diagnostics read it too; the backward scan reuses the
+// control block and status words after the forward scan), the backward scan's records
+// (two carries of five tagged 64-bit words per tile and channel), then float32 planes of
+// [n_chunks][n_lanes]: 3 for the forward states entering each tile, 2 for partial sums.
+constexpr int kBwdPlanes = 3 + 2;
 
 struct BwdLayout {
     ChunkLayout fwd;
-    size_t off_planes, plane_bytes, total;
+    size_t off_rrecs, off_planes, plane_bytes, total;
 };
 
 BwdLayout backward_layout(int64_t B, int64_t T, int64_t C) {
     BwdLayout L;
     L.fwd = chunked_layout(B, T, C, wkv::kBwdTile);
     const int64_t n_lanes = B * ceil_div(C, 64) * 64;
-    L.plane_bytes = align_up((size_t)ceil_div(T, wkv::kBwdTile) * (size_t)n_lanes * 4, kAlign);
-    L.off_planes = align_up(L.fwd.total, kAlign);
+    const int64_t n_chunks = ceil_div(T, wkv::kBwdTile);
+    const size_t n_tiles = (size_t)(n_lanes / 64) * (size_t)n_chunks;
+    L.off_rrecs = align_up(L.fwd.total, kAlign);
+    L.off_planes = L.off_rrecs + align_up(n_tiles * 2 * 5 * 64 * 8, kAlign);
+    L.plane_bytes = align_up((size_t)n_chunks * (size_t)n_lanes * 4, kAlign);
     L.total = L.off_planes + kBwdPlanes * L.plane_bytes;
     return L;
 }
@@ -287,10 +291,11 @@ wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.fw_a = planes;
     a.fw_b = planes + ps;
     a.fw_p = planes + 2 * ps;
-    a.rv = planes + 3 * ps;
-    a.rin = planes + 8 * ps;
-    a.part = planes + 13 * ps;
+    a.part = planes + 3 * ps;
     a.plane = (long)ps;
+    a.ctrl = f.ctrl;
+    a.status = f.status;
+    a.rrecs = base + L.off_rrecs;
     a.B = (int)B;
     a.T = (int)T;
     a.C = (int)C;
@@ -298,7 +303,9 @@ wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.n_groups = (int)n_groups;
     a.n_chunks = (int)n_chunks;
     a.n_lanes = (long)(n_groups * 64);
-    return wkv::launch_bwd(a, dt == WKV_F32 ? 0 : 1, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+    int io = chunk_io(dt, C, k, v, gy);
+    if (io == wkv::kIoBf16Pair && !(aligned(gk, 4) && aligned(gv, 4))) io = wkv::kIoBf16;
+    return wkv::launch_bwd(a, io, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

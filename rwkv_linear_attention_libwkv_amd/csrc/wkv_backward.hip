@@ -18,18 +18,20 @@
 //
 // Plan (tiles of kBwdTile tokens x 64 channels, aligned with the forward tiles):
 //   1. the chunked forward kernel dumps the forward state entering every tile;
-//   2. bwd_tile_kernel<pass 0>: per tile, recompute y and q from that state and reduce
-//      the tile to its reverse aggregate (G, H, G', H' it contributes before its start);
-//   3. bwd_carry_kernel: per lane, a backwards scan over the tiles' aggregates gives the
-//      reverse carry entering every tile from the right;
-//   4. bwd_tile_kernel<pass 1>: per tile, recompute again and walk the tokens backwards
-//      from that carry, writing dL/dk, dL/dv and per-tile dL/dw, dL/du partials;
-//   5. bwd_reduce_kernel: per lane, sum the partials.
-// Every step is a deterministic function of its inputs (no atomics), so gradients are
-// bitwise reproducible.
+//   2. bwd_scan_kernel, a single-pass chained scan backwards in time: per tile, recompute
+//      y and q from the dumped state, reduce the tile to its reverse aggregate (the G, H,
+//      G', H' it contributes before its start), publish it, find the reverse carry
+//      entering from the right by decoupled look-back over the later tiles, publish the
+//      inclusive carry, then walk the tokens backwards writing dL/dk, dL/dv and the
+//      tile's dL/dw, dL/du partial sums;
+//   3. bwd_reduce_kernel: per lane, sum the partials in a fixed order.
+// Every result is a deterministic function of the inputs (the carries follow one
+// canonical chain of operations whichever record a look-back starts from, and no sum
+// uses atomics), so gradients are bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wkv_chain.h"
 #include "wkv_device.h"
 #include "wkv_kernels.h"
 #include "wkv_rows.h"
@@ -70,18 +72,19 @@ __device__ __forceinline__ Rev normalize_rev(const Rev& c) {
             __builtin_ldexpf(c.hp, -e), c.r + (double)e};
 }
 
-// float32 storage form: reference rounded to float32, the exact residual folded in.
-__device__ __forceinline__ void store_rev(float* base, size_t plane, size_t i, const Rev& c) {
+// The float32 form a carry takes in a record: float32 reference rf and the exact
+// residual factor 2^(r - rf) folded into the sums (the same values up to one rounding).
+__device__ __forceinline__ Rev rev_rec_form(const Rev& c) {
     const float rf = fmaxf((float)c.r, -3.0e38f);
     const float f = ex2((float)(c.r - (double)rf));
-    base[i] = c.g * f;
-    base[plane + i] = c.h * f;
-    base[2 * plane + i] = c.gp * f;
-    base[3 * plane + i] = c.hp * f;
-    base[4 * plane + i] = rf;
+    return {c.g * f, c.h * f, c.gp * f, c.hp * f, (double)rf};
 }
-__device__ __forceinline__ Rev load_rev(const float* base, size_t plane, size_t i) {
-    return {base[i], base[plane + i], base[2 * plane + i], base[3 * plane + i], (double)base[4 * plane + i]};
+
+// One link of the canonical chain of inclusive carries: the carry entering the later
+// tile (record form) folded through a tile of n tokens whose aggregate is `agg` (record
+// form).  Tiles and look-backs compute inclusive carries with exactly these operations.
+__device__ __forceinline__ Rev advance_rev(const Rev& later, const Rev& agg, int n, double w2) {
+    return rev_rec_form(fold_rev(agg, normalize_rev(later), n, w2));
 }
 
 // Fast path of one wave's L tokens in the frame of reference R (log2 units): x_j =
@@ -91,18 +94,73 @@ template <int L>
 struct BwdChunk {
     float k[L], v[L], g[L], y[L];
 
+    // rows at or beyond nv (wave-uniform) and lanes with !valid read as zero
     template <typename IO>
     __device__ __forceinline__ void load(const WaveRows& w, Rsrc gy, int nv, bool valid) {
+        if constexpr (kPair<IO>) {
+            // row pairs: every 4-byte load first, then the exchanges with the partner lane
+            // (all 64 lanes take part in those; only the loads are predicated)
+            uint32_t xk[L / 2], xv[L / 2], xg[L / 2];
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            k[j] = 0.f;
-            v[j] = 0.f;
-            g[j] = 0.f;
-            if (j < nv && valid) {
-                const uint32_t so = (uint32_t)j * w.row_bytes;
-                k[j] = load_elt<IO>(w.k, w.lane_off, so);
-                v[j] = load_elt<IO>(w.v, w.lane_off, so);
-                g[j] = load_elt<IO>(gy, w.lane_off, so);
+            for (int jj = 0; jj < L / 2; ++jj) {
+                xk[jj] = 0u;
+                xv[jj] = 0u;
+                xg[jj] = 0u;
+                if (valid && 2 * jj + (int)w.upper < nv) {
+                    const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
+                    xk[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.k, w.pair_off, so, kStream);
+                    xv[jj] = __builtin_amdgcn_raw_buffer_load_b32(w.v, w.pair_off, so, kStream);
+                    xg[jj] = __builtin_amdgcn_raw_buffer_load_b32(gy, w.pair_off, so, kStream);
+                }
+            }
+            const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+            for (int jj = 0; jj < L / 2; ++jj) {
+                const uint32_t pk = pair_exchange(xk[jj], w.partner, sel);
+                const uint32_t pv = pair_exchange(xv[jj], w.partner, sel);
+                const uint32_t pg = pair_exchange(xg[jj], w.partner, sel);
+                k[2 * jj] = bf_lo(pk);
+                k[2 * jj + 1] = bf_hi(pk);
+                v[2 * jj] = bf_lo(pv);
+                v[2 * jj + 1] = bf_hi(pv);
+                g[2 * jj] = bf_lo(pg);
+                g[2 * jj + 1] = bf_hi(pg);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                k[j] = 0.f;
+                v[j] = 0.f;
+                g[j] = 0.f;
+                if (j < nv && valid) {
+                    const uint32_t so = (uint32_t)j * w.row_bytes;
+                    k[j] = load_elt<IO>(w.k, w.lane_off, so);
+                    v[j] = load_elt<IO>(w.v, w.lane_off, so);
+                    g[j] = load_elt<IO>(gy, w.lane_off, so);
+                }
+            }
+        }
+    }
+    // dL/dk (in k) and dL/dv (in v) of a full chunk, after backward()
+    template <typename IO>
+    __device__ __forceinline__ void store_grads(const WaveRows& w, Rsrc gk, Rsrc gv, bool valid) const {
+        if constexpr (kPair<IO>) {
+            const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+            for (int jj = 0; jj < L / 2; ++jj) {
+                const uint32_t wk = pair_exchange(pack_bf16(k[2 * jj], k[2 * jj + 1]), w.partner, sel);
+                const uint32_t wv = pair_exchange(pack_bf16(v[2 * jj], v[2 * jj + 1]), w.partner, sel);
+                if (valid) {
+                    const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
+                    __builtin_amdgcn_raw_buffer_store_b32(wk, gk, w.pair_off, so, kStream);
+                    __builtin_amdgcn_raw_buffer_store_b32(wv, gv, w.pair_off, so, kStream);
+                }
+            }
+        } else if (valid) {
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                store_elt<IO>(gk, w.lane_off, (uint32_t)j * w.row_bytes, k[j]);
+                store_elt<IO>(gv, w.lane_off, (uint32_t)j * w.row_bytes, v[j]);
             }
         }
     }
@@ -152,6 +210,25 @@ struct BwdChunk {
             H = fmaf(ch.d, H, g[j] * y[j]);
         }
         return Rev{G, H, Gp, Hp, -(double)R};
+    }
+    // wave 0 parks its chunk in LDS while it runs the look-back (keeps registers free)
+    __device__ __forceinline__ void stash(float (*st)[64], int lane) const {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            st[j][lane] = k[j];
+            st[L + j][lane] = v[j];
+            st[2 * L + j][lane] = g[j];
+            st[3 * L + j][lane] = y[j];
+        }
+    }
+    __device__ __forceinline__ void unstash(float (*st)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            k[j] = st[j][lane];
+            v[j] = st[L + j][lane];
+            g[j] = st[2 * L + j][lane];
+            y[j] = st[3 * L + j][lane];
+        }
     }
     // gradients from the reverse carry at the wave's last position; k, v are replaced
     // by dL/dk, dL/dv; accumulates the lane's dL/dw, dL/du
@@ -236,6 +313,7 @@ __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, cons
 // Everything a tile's waves share.
 template <int NW>
 struct BwdShared {
+    int ticket;
     float a[NW][64];  // forward: per-wave aggregate, then the state before each wave
     float b[NW][64];
     double p[NW][64];
@@ -246,13 +324,87 @@ struct BwdShared {
     double r[NW][64];
     float gw[NW][64];  // per-wave partial sums
     float gu[NW][64];
+    float stash[4 * (kBwdTile / NW)][64];  // wave 0's chunk while it runs the look-back
 };
 
 // Fast-path bound for the reverse carry in a wave's frame: G^ = g 2^(r + R) with |g| < 1.
 constexpr float kSpanRev = 60.f;
 
-template <typename IO, int L, int NW, int PASS>
-__global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
+// Records of the backward scan: rec[chunk][g][slot][comp][lane] (u64; slot 0 the tile's
+// reverse aggregate, slot 1 the inclusive carry at the tile's start; comp = g, h, gp, hp,
+// r), status[g][chunk] as in the forward scan.
+struct RevRecs {
+    uint64_t* rec;       // records of chunk 0 of this group
+    uint32_t* status;    // this group's status words
+    size_t chunk_words;  // words per chunk index over all groups: n_groups * 10 * 64
+    uint32_t tag_agg, tag_incl;
+    uint32_t give_up_word;
+    __device__ __forceinline__ uint64_t* word(int chunk, int slot, int comp, int lane) const {
+        return rec + (size_t)chunk * chunk_words + (size_t)(slot * 5 + comp) * 64 + lane;
+    }
+};
+
+__device__ __forceinline__ void publish_rev(const RevRecs& R, int chunk, int slot, int lane, const Rev& c,
+                                            uint32_t tag) {
+    st_word(R.word(chunk, slot, 0, lane), c.g, tag);
+    st_word(R.word(chunk, slot, 1, lane), c.h, tag);
+    st_word(R.word(chunk, slot, 2, lane), c.gp, tag);
+    st_word(R.word(chunk, slot, 3, lane), c.hp, tag);
+    st_word(R.word(chunk, slot, 4, lane), (float)c.r, tag);
+    if (lane == 0) __hip_atomic_store(&R.status[chunk], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The carry entering chunk ci from the right (ci < n_chunks - 1): folded from the
+// nearest inclusive record on the right through the aggregates between, in chunk order
+// from right to left, with advance_rev (every chunk between is a full tile).  Each
+// round re-reads its words until every tag matches; gives up like the forward scan.
+template <int TILE>
+__device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs& R, double w2, int ci, int lane,
+                                              Rev& out) {
+    const int start = find_inclusive<1>(R.status, args.n_chunks, ci, lane, R.tag_agg, R.tag_incl, args.ctrl,
+                                        R.give_up_word);
+    if (start < 0) return false;
+    Rev P{0.f, 0.f, 0.f, 0.f, 0.0};
+    bool have_p = false;
+#pragma unroll 1
+    for (int c0 = start - 1;; --c0) {
+        uint64_t inc[5], t[5];
+        const bool need_agg = c0 > ci;
+        for (uint32_t spin = 0;; ++spin) {
+            bool good = true;
+            if (!have_p)
+#pragma unroll
+                for (int q = 0; q < 5; ++q) {
+                    inc[q] = ld_word(R.word(start, 1, q, lane));
+                    good = good && word_tag(inc[q]) == R.tag_incl;
+                }
+            if (need_agg)
+#pragma unroll
+                for (int q = 0; q < 5; ++q) {
+                    t[q] = ld_word(R.word(c0, 0, q, lane));
+                    good = good && word_tag(t[q]) == R.tag_agg;
+                }
+            if (__all(good)) break;
+            if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
+            __builtin_amdgcn_s_sleep(kPollSleep);
+        }
+        if (!have_p) {
+            P = Rev{word_val(inc[0]), word_val(inc[1]), word_val(inc[2]), word_val(inc[3]), (double)word_val(inc[4])};
+            have_p = true;
+        }
+        if (!need_agg) break;
+        P = advance_rev(P, Rev{word_val(t[0]), word_val(t[1]), word_val(t[2]), word_val(t[3]), (double)word_val(t[4])},
+                        TILE, w2);
+    }
+    out = P;
+    return true;
+}
+
+// One tile of the backward scan (see the plan at the top).  Tiles are numbered in the
+// order workgroups start, from the last chunk of the sequence to the first, so every
+// tile this one waits on has started and publishes its aggregate without waiting.
+template <typename IO, int L, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     constexpr int TILE = L * NW;
     static_assert(TILE == kBwdTile, "tiles must line up with the dumped forward tiles");
     const int lane = threadIdx.x & 63;
@@ -260,17 +412,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
     const int C = args.C, T = args.T;
     __shared__ BwdShared<NW> sh;
 
-    const int g = blockIdx.x % args.n_groups;
-    const int ci = blockIdx.x / args.n_groups;
+    if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
+    const int g = ticket % args.n_groups;
+    const int ci = args.n_chunks - 1 - ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
     const int c_grp = (g - bi * args.groups_per_row) * 64;
-    const int c = c_grp + lane;
+    const int c = c_grp + (kPair<IO> ? pair_channel(lane) : lane);
     const bool cvalid = c < C;
     const int t_tile = ci * TILE;
+    const int tile_len = min(TILE, T - t_tile);
     const int t0 = __builtin_amdgcn_readfirstlane(t_tile + wid * L);
     const int nv = max(0, min(L, T - t0));
-    const size_t li = (size_t)g * 64 + lane;                  // lane index
-    const size_t ti = (size_t)ci * args.n_lanes + li;         // (tile, lane) index
+    const size_t li = (size_t)g * 64 + (c - c_grp);    // lane index (this lane's channel)
+    const size_t ti = (size_t)ci * args.n_lanes + li;  // (tile, lane) index
     const size_t plane = (size_t)args.plane;
 
     WaveRows rows;
@@ -278,14 +434,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
     rows.k = make_rsrc(static_cast<const char*>(args.k) + off);
     rows.v = make_rsrc(static_cast<const char*>(args.v) + off);
     rows.y = make_rsrc(static_cast<char*>(args.gk) + off);  // unused by the row helpers here
-    rows.lane_off = (uint32_t)(lane * sizeof(IO));
+    rows.lane_off = (uint32_t)((c - c_grp) * sizeof(IO));
     rows.row_bytes = (uint32_t)(C * sizeof(IO));
+    rows.pair_off = (uint32_t)((lane & 31) * 4) + (uint32_t)(lane >> 5) * rows.row_bytes;
+    rows.upper = (uint32_t)(lane >> 5);
+    rows.partner = (uint32_t)((lane ^ 32) << 2);
     const Rsrc gyr = make_rsrc(static_cast<const char*>(args.gy) + off);
     const Rsrc gkr = make_rsrc(static_cast<char*>(args.gk) + off);
     const Rsrc gvr = make_rsrc(static_cast<char*>(args.gv) + off);
 
     BwdChunk<L> ck;
     ck.template load<IO>(rows, gyr, nv, cvalid);
+
+    // read after the loads are issued; constant during the launch
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
+    RevRecs recs;
+    recs.rec = static_cast<uint64_t*>(args.rrecs) + (size_t)g * 10 * 64;
+    recs.chunk_words = (size_t)args.n_groups * 10 * 64;
+    recs.status = args.status + (size_t)g * args.n_chunks;
+    recs.tag_agg = (epoch << 2) | kKindAgg;
+    recs.tag_incl = (epoch << 2) | kKindIncl;
+    recs.give_up_word = epoch | kCtrlGiveUpMark;
 
     const Chan ch = make_chan(args.w[cvalid ? c : 0], args.u[cvalid ? c : 0]);
     const double w2 = w2_of(ch);
@@ -338,9 +507,25 @@ __global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
     sh.r[wid][lane] = ragg.r;
     __syncthreads();
 
-    // ---- combine backwards: the carry after each wave (pass 1) or the tile aggregate ----
+    // ---- wave 0: tile aggregate, look-back, publish, carry after each wave ----
     if (wid == 0) {
-        Rev run = PASS == 0 ? empty_rev() : normalize_rev(load_rev(args.rin, plane, ti));
+        ck.stash(sh.stash, lane);
+        asm volatile("" ::: "memory");  // the chunk must really leave the registers
+        Rev run = empty_rev();
+#pragma unroll 1
+        for (int wv = NW - 1; wv >= 0; --wv) {
+            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
+            const Rev rw{sh.g[wv][lane], sh.h[wv][lane], sh.gp[wv][lane], sh.hp[wv][lane], sh.r[wv][lane]};
+            run = normalize_rev(fold_rev(rw, run, nvw, w2));
+        }
+        const Rev agg_rec = rev_rec_form(run);
+        Rev rin = rev_rec_form(empty_rev());
+        if (ci + 1 < args.n_chunks) {
+            publish_rev(recs, ci, 0, lane, agg_rec, recs.tag_agg);
+            if (!rev_look_back<TILE>(args, recs, w2, ci, lane, rin)) rin = rev_rec_form(empty_rev());
+        }
+        if (ci > 0) publish_rev(recs, ci, 1, lane, advance_rev(rin, agg_rec, tile_len, w2), recs.tag_incl);
+        run = normalize_rev(rin);
 #pragma unroll 1
         for (int wv = NW - 1; wv >= 0; --wv) {
             const int nvw = max(0, min(L, T - (t_tile + wv * L)));
@@ -352,22 +537,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
             sh.r[wv][lane] = run.r;
             run = normalize_rev(fold_rev(rw, run, nvw, w2));
         }
-        if (PASS == 0) store_rev(args.rv, plane, ti, run);
+        asm volatile("" ::: "memory");
+        ck.unstash(sh.stash, lane);
     }
-    if (PASS == 0) return;
     __syncthreads();
 
-    // ---- pass 1: gradients of this wave's tokens from the carry after the wave ----
+    // ---- gradients of this wave's tokens from the carry after the wave ----
     const Rev cin{sh.g[wid][lane], sh.h[wid][lane], sh.gp[wid][lane], sh.hp[wid][lane], sh.r[wid][lane]};
     if (wave_fast && __all(cin.r + (double)R <= (double)kSpanRev)) {
         ck.backward(ch, cin, R, gw, gu);
-        if (cvalid) {
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                store_elt<IO>(gkr, rows.lane_off, (uint32_t)j * rows.row_bytes, ck.k[j]);
-                store_elt<IO>(gvr, rows.lane_off, (uint32_t)j * rows.row_bytes, ck.v[j]);
-            }
-        }
+        ck.template store_grads<IO>(rows, gkr, gvr, cvalid);
     } else {
         gw = 0.f;
         gu = 0.f;
@@ -386,38 +565,39 @@ __global__ __launch_bounds__(64 * NW) void bwd_tile_kernel(BwdArgs args) {
         args.part[ti] = sw;
         args.part[plane + ti] = su;
     }
+    // ---- launch bookkeeping (a give-up of the forward scan before is carried over) ----
+    if (threadIdx.x == 0) finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, true);
 }
 
-// Per lane, backwards over the tiles: the carry entering each tile from the right.
-__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs args) {
-    const long li = (long)blockIdx.x * 256 + threadIdx.x;
-    if (li >= args.n_lanes) return;
-    const int g = (int)(li / 64);
-    const int c = (g % args.groups_per_row) * 64 + (int)(li % 64);
-    const double w2 = (double)args.w[c < args.C ? c : 0] * kLog2eD;
-    const size_t plane = (size_t)args.plane;
-    Rev run = empty_rev();
-    for (int ci = args.n_chunks - 1; ci >= 0; --ci) {
-        const size_t ti = (size_t)ci * args.n_lanes + li;
-        store_rev(args.rin, plane, ti, run);
-        const int n = min(kBwdTile, args.T - ci * kBwdTile);
-        run = normalize_rev(fold_rev(normalize_rev(load_rev(args.rv, plane, ti)), run, n, w2));
-    }
-}
+// dL/dw and dL/du per lane: the tiles' partials summed in a fixed order.  Block: 64 lanes
+// x kRedSlices slices; slice s sums chunks s, s + kRedSlices, ...; slice 0 then adds the
+// slices' sums in order.
+constexpr int kRedSlices = 16;
 
-// Per lane: dL/dw and dL/du as the sums of the tiles' partials.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs args) {
-    const long li = (long)blockIdx.x * 256 + threadIdx.x;
-    if (li >= args.n_lanes) return;
-    const int g = (int)(li / 64);
-    const int bi = g / args.groups_per_row;
-    const int c = (g % args.groups_per_row) * 64 + (int)(li % 64);
-    if (c >= args.C) return;
+__global__ __launch_bounds__(64 * kRedSlices) void bwd_reduce_kernel(BwdArgs args) {
+    __shared__ float sw_s[kRedSlices][64], su_s[kRedSlices][64];
+    const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
+    const long li = (long)blockIdx.x * 64 + lane;
     const size_t plane = (size_t)args.plane;
     float sw = 0.f, su = 0.f;
-    for (int ci = 0; ci < args.n_chunks; ++ci) {
+    for (int ci = slice; ci < args.n_chunks; ci += kRedSlices) {
         sw += args.part[(size_t)ci * args.n_lanes + li];
         su += args.part[plane + (size_t)ci * args.n_lanes + li];
+    }
+    sw_s[slice][lane] = sw;
+    su_s[slice][lane] = su;
+    __syncthreads();
+    if (slice != 0) return;
+    const int g = (int)(li / 64);
+    const int bi = g / args.groups_per_row;
+    const int c = (g % args.groups_per_row) * 64 + lane;
+    if (c >= args.C) return;
+    sw = 0.f;
+    su = 0.f;
+#pragma unroll
+    for (int s = 0; s < kRedSlices; ++s) {
+        sw += sw_s[s][lane];
+        su += su_s[s][lane];
     }
     args.gw[(size_t)bi * args.C + c] = sw;
     args.gu[(size_t)bi * args.C + c] = su;
@@ -427,16 +607,15 @@ template <typename IO>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     constexpr int L = 16, NW = kBwdTile / L;
     const unsigned tiles = (unsigned)((long)a.n_groups * a.n_chunks);
-    const unsigned lane_blocks = (unsigned)((a.n_lanes + 255) / 256);
-    hipLaunchKernelGGL((bwd_tile_kernel<IO, L, NW, 0>), dim3(tiles), dim3(64 * NW), 0, s, a);
-    hipLaunchKernelGGL(bwd_carry_kernel, dim3(lane_blocks), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bwd_tile_kernel<IO, L, NW, 1>), dim3(tiles), dim3(64 * NW), 0, s, a);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(lane_blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<IO, L, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.n_groups), dim3(64 * kRedSlices), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_bwd_t<float>(a, s) : launch_bwd_t<uint16_t>(a, s);
+hipError_t launch_bwd(const BwdArgs& a, int io, hipStream_t s) {
+    if (io == kIoF32) return launch_bwd_t<float>(a, s);
+    if (io == kIoBf16Pair) return launch_bwd_t<Bf16Pair>(a, s);
+    return launch_bwd_t<uint16_t>(a, s);
 }
 
 }  // namespace wkv

@@ -28,6 +28,7 @@
 
 #include "wkv_device.h"
 #include "wkv_kernels.h"
+#include "wkv_chain.h"
 #include "wkv_rows.h"
 
 namespace wkv {
@@ -335,9 +336,6 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
 // end, and the last one resets both counters and advances the epoch for the next
 // launch (every other workgroup has read the epoch and taken its ticket by then).
 
-constexpr uint32_t kKindAgg = 1u;
-constexpr uint32_t kKindIncl = 2u;
-constexpr uint32_t kMaxSpins = 1u << 18;
 // Aggregate records a look-back loads per round of its forward fold.  Registers for the
 // batch are reserved by every wave (the look-back's code path shares the allocation with
 // the waves that keep their chunk), so the batch is one record: float32 tiles fold 0.3
@@ -345,7 +343,6 @@ constexpr uint32_t kMaxSpins = 1u << 18;
 // C=5120), and a batch of two measured no faster.
 template <typename IO>
 constexpr int fold_batch() { return 1; }
-constexpr int kPollSleep = 2;  // s_sleep between polls (units of 64 clocks)
 
 struct TileRecs {
     uint64_t* rec;       // records of chunk 0 of this group
@@ -357,16 +354,6 @@ struct TileRecs {
         return rec + (size_t)chunk * chunk_words + (size_t)(slot * 3 + comp) * 64 + lane;
     }
 };
-
-__device__ __forceinline__ void st_word(uint64_t* p, float v, uint32_t tag) {
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 32); }
-__device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // Publish the record of `slot` for this lane's channel, then the tile's status hint.
 __device__ __forceinline__ void publish(const TileRecs& R, int chunk, int slot, int lane, const Carry& c,
@@ -393,19 +380,6 @@ __device__ __forceinline__ Carry advance(const Carry& prev, const Carry& agg, do
     return rec_form(combine(normalize(prev), agg, decay));
 }
 
-// Raise this launch's give-up word (once per wave) and report failure.
-__device__ __forceinline__ bool give_up(const FwdArgs& args, const TileRecs& R, int lane) {
-    if (lane == 0)
-        __hip_atomic_store(&args.ctrl[kCtrlGiveUp], R.give_up_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return false;
-}
-
-__device__ __forceinline__ bool should_stop(const FwdArgs& args, const TileRecs& R, uint32_t spin) {
-    if (spin >= kMaxSpins) return true;
-    return (spin & 31u) == 31u &&
-           __hip_atomic_load(&args.ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == R.give_up_word;
-}
-
 // The state entering chunk ci (ci >= 1): lane l inspects the status of chunk ci-1-l,
 // 64 chunks per window, until the nearest inclusive record is found with every chunk
 // after it published; the state is then folded forward from that inclusive record
@@ -415,36 +389,9 @@ __device__ __forceinline__ bool should_stop(const FwdArgs& args, const TileRecs&
 template <int TILE, int FB>
 __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan& ch, int ci,
                                           int lane, Carry& out) {
-    int nearest = ci - 1;  // chunk inspected by lane 0 in the current window
-    int start = -1;        // chunk holding the nearest inclusive record
-    for (;;) {
-        const int pc = nearest - lane;
-        const int nlanes = min(64, nearest + 1);
-        bool window_done = false;
-        for (uint32_t spin = 0;; ++spin) {
-            const uint32_t st =
-                pc >= 0 ? __hip_atomic_load(&R.status[pc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-            const bool is_incl = pc >= 0 && st == R.tag_incl;
-            const bool is_ready = is_incl || (pc >= 0 && st == R.tag_agg);
-            const uint64_t incl = __ballot(is_incl);
-            const uint64_t ready = __ballot(is_ready);
-            if (incl) {
-                const int d = __builtin_ctzll(incl);
-                const uint64_t need = (d >= 63) ? ~0ull : ((2ull << d) - 1ull);
-                if ((ready & need) == need) {
-                    start = nearest - d;
-                    break;
-                }
-            } else if (nlanes == 64 && ready == ~0ull) {
-                window_done = true;  // 64 aggregates, no inclusive record yet: look further back
-                break;
-            }
-            if (should_stop(args, R, spin)) return give_up(args, R, lane);
-            __builtin_amdgcn_s_sleep(kPollSleep);
-        }
-        if (!window_done) break;
-        nearest -= 64;
-    }
+    const int start = find_inclusive<-1>(R.status, args.n_chunks, ci, lane, R.tag_agg, R.tag_incl, args.ctrl,
+                                         R.give_up_word);
+    if (start < 0) return false;
     // fold forward from the inclusive record of `start` through the aggregates after it,
     // FB aggregates per round; the first round also loads the inclusive record, and a
     // round re-reads its words until every tag matches
@@ -472,7 +419,7 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
                         good = good && word_tag(t[j][q]) == R.tag_agg;
                     }
             if (__all(good)) break;
-            if (should_stop(args, R, spin)) return give_up(args, R, lane);
+            if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
         if (!have_p) {
@@ -655,16 +602,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
 
     // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t n_tiles = (uint32_t)args.n_groups * (uint32_t)args.n_chunks;
-        const uint32_t done = atomicAdd(&args.ctrl[kCtrlDone], 1u);
-        if (done + 1u == n_tiles) {
-            __hip_atomic_store(&args.ctrl[kCtrlTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&args.ctrl[kCtrlDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&args.ctrl[kCtrlEpoch], (epoch + 1u) & kCtrlEpochMask, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (threadIdx.x == 0) finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, false);
 }
 
 // Zero a workspace (the state every workspace must start from).

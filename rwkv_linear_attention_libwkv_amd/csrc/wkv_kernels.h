@@ -57,8 +57,9 @@ hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
                              float* ob, float* op, long n, hipStream_t s);
 
-// Backward of the chunked forward (gradients of sum(gy * y)), in tiles of kBwdTile tokens
-// x 64 channels that line up with the forward tiles whose entering states were dumped.
+// Backward (gradients of sum(gy * y)): a chained scan backwards in time over tiles of
+// kBwdTile tokens x 64 channels that line up with the forward tiles whose entering states
+// the forward kernel dumped.
 constexpr int kBwdTile = 128;
 struct BwdArgs {
     const float* w;
@@ -66,22 +67,24 @@ struct BwdArgs {
     const void* k;   // [B, T, C] dtype
     const void* v;
     const void* gy;  // dL/dy
-    void* gk;        // [B, T, C] dtype, written by pass 1
+    void* gk;        // [B, T, C] dtype
     void* gv;
     float* gw;       // [B, C] per-lane dL/dw, written by the reduction
     float* gu;
     const float* fw_a;  // [n_chunks][n_lanes] forward state entering each tile (dump)
     const float* fw_b;
     const float* fw_p;
-    float* rv;       // [5][n_chunks][n_lanes] reverse aggregate of each tile (pass 0)
-    float* rin;      // [5][n_chunks][n_lanes] reverse carry entering each tile from the right
-    float* part;     // [2][n_chunks][n_lanes] per-tile dL/dw, dL/du partial sums
-    long plane;      // float stride between the planes of fw_*, rv, rin, part (>= n_chunks * n_lanes)
+    float* part;        // [2][n_chunks][n_lanes] per-tile dL/dw, dL/du partial sums
+    long plane;         // float stride between the planes of fw_* and part (>= n_chunks * n_lanes)
+    uint32_t* ctrl;     // control block (shared with the forward scan, which runs first)
+    uint32_t* status;   // [n_groups][n_chunks] status hints
+    void* rrecs;        // [n_chunks][n_groups][2][5][64] tagged 64-bit words
     int B, T, C;
     int groups_per_row, n_groups, n_chunks;
-    long n_lanes;    // n_groups * 64
+    long n_lanes;       // n_groups * 64
 };
-hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t s);
+// io: IoMode of k, v, gy, gk, gv (row pairs need even C and 4-byte aligned arrays).
+hipError_t launch_bwd(const BwdArgs& a, int io, hipStream_t s);
 
 struct StepArgs {
     const float* w;  // [G, C]

@@ -153,9 +153,9 @@ def test_backward_workspace_query():
     assert q(0, 4, 4, F32) == 0 and q(4, 0, 4, F32) == 0
     a = q(8, 8192, 2048, F32)
     assert a == q(8, 8192, 2048, BF16)
-    # about 0.47 bytes per element plus the forward records (0.375 per element at 128)
+    # per 128 x 64 tile: 3 + 5 tagged 8-byte words x 2 slots x 64 channels, 5 float32 planes
     elems = 8 * 8192 * 2048
-    assert 0.8 * elems < a < 0.9 * elems + (1 << 20)
+    assert 1.1 * elems < a < 1.2 * elems + (1 << 20)
     # it holds a forward chunked workspace at chunk length 128
     assert a > lib.wkv_forward_workspace_bytes(8, 8192, 2048, F32, 2, 128)
 

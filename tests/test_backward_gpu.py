@@ -57,7 +57,7 @@ def run_backward(dev, workspace=None):
     out = libwkv.wkv_backward(dev["w"], dev["u"], dev["k"], dev["v"], dev["gy"], workspace=ws)
     torch.cuda.synchronize()
     if ws is not None:
-        assert libwkv.lookback_error(ws) == 0, "the forward scan gave up waiting"
+        assert libwkv.lookback_error(ws) == 0, "a scan gave up waiting"
     return [host(x) for x in out]
 
 
@@ -190,3 +190,31 @@ def test_long_sequence_sampled_lanes():
             err = grad_error(g, ref[i], scale[i])
             print(f"    lane ({b},{c}) {name}: {err:.3e}", flush=True)
             assert err <= TOL_F32, (b, c, name, err)
+
+
+def test_workspace_epoch_advances_twice_per_call():
+    """Each call runs two chained scans on the workspace's control block (forward, then
+    backward in time); neither gives up."""
+    inp = grad_inputs(2, 1000, 130, seed=13)
+    dev = to_device(inp)
+    ws = libwkv.new_backward_workspace(2, 1000, 130)
+    for i in range(3):
+        run_backward(dev, ws)
+        gave_up, epoch = libwkv.workspace_query(ws)
+        assert gave_up == 0 and epoch == 2 * (i + 1), (gave_up, epoch)
+
+
+def test_bf16_row_pairs_match_two_byte_lanes():
+    """Even C with 4-byte aligned arrays moves bfloat16 rows in pairs; a gk that is only
+    2-byte aligned takes 2-byte lanes.  The arithmetic per channel is the same, so the
+    gradients must agree bit for bit."""
+    inp = grad_inputs(2, 700, 192, seed=31, dtype="bf16", k_std=1.5)
+    dev = to_device(inp)
+    pair = libwkv.wkv_backward(dev["w"], dev["u"], dev["k"], dev["v"], dev["gy"])
+    buf = torch.empty(dev["k"].numel() + 1, dtype=torch.bfloat16, device="cuda")
+    gk_odd = buf[1:].view(dev["k"].shape)
+    assert gk_odd.data_ptr() % 4 == 2
+    lanes = libwkv.wkv_backward(dev["w"], dev["u"], dev["k"], dev["v"], dev["gy"], gk=gk_odd)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, pair, lanes):
+        assert torch.equal(a, b), name
