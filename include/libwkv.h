@@ -161,9 +161,9 @@ wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
 
 /*
  * Bytes of device workspace that wkv_backward needs for this problem (0 for
- * empty problems, (size_t)-1 for invalid arguments): about 1.16 bytes per
- * element of k (the records of the forward and backward scans over tiles of
- * 128 time steps, and five float32 values per tile and channel).
+ * empty problems, (size_t)-1 for invalid arguments): about one byte per
+ * element of k (the records of a forward scan and of a backward scan over
+ * tiles of 128 time steps, and five float32 values per such tile and channel).
  */
 size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt);
 

@@ -137,25 +137,29 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     return wkv::launch_fwd_chunked(a, io, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
-// Workspace of the backward: the forward chunked workspace at kBwdTile (its control
-// block first, so the forward diagnostics read it too; the backward scan reuses the
-// control block and status words after the forward scan), the backward scan's records
-// (two carries of five tagged 64-bit words per tile and channel), then float32 planes of
-// [n_chunks][n_lanes]: 3 for the forward states entering each tile, 2 for partial sums.
+// Workspace of the backward: the forward chunked workspace at the forward's default tile
+// (its control block first, so the forward diagnostics read it too; the backward scan
+// reuses the control block after the forward scan), the backward scan's status words and
+// records (two carries of five tagged 64-bit words per kBwdTile tile and channel), then
+// float32 planes of [n_chunks][n_lanes]: 3 for the forward states entering each tile,
+// 2 for partial sums.
 constexpr int kBwdPlanes = 3 + 2;
 
 struct BwdLayout {
+    int fwd_tile;
     ChunkLayout fwd;
-    size_t off_rrecs, off_planes, plane_bytes, total;
+    size_t off_status, off_rrecs, off_planes, plane_bytes, total;
 };
 
 BwdLayout backward_layout(int64_t B, int64_t T, int64_t C) {
     BwdLayout L;
-    L.fwd = chunked_layout(B, T, C, wkv::kBwdTile);
+    L.fwd_tile = default_tile(B, T, C);
+    L.fwd = chunked_layout(B, T, C, L.fwd_tile);
     const int64_t n_lanes = B * ceil_div(C, 64) * 64;
     const int64_t n_chunks = ceil_div(T, wkv::kBwdTile);
     const size_t n_tiles = (size_t)(n_lanes / 64) * (size_t)n_chunks;
-    L.off_rrecs = align_up(L.fwd.total, kAlign);
+    L.off_status = align_up(L.fwd.total, kAlign);
+    L.off_rrecs = L.off_status + align_up(n_tiles * 4, kAlign);
     L.off_planes = L.off_rrecs + align_up(n_tiles * 2 * 5 * 64 * 8, kAlign);
     L.plane_bytes = align_up((size_t)n_chunks * (size_t)n_lanes * 4, kAlign);
     L.total = L.off_planes + kBwdPlanes * L.plane_bytes;
@@ -267,14 +271,14 @@ wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     f.C = (int)C;
     f.groups_per_row = groups_per_row;
     f.n_groups = (int)n_groups;
-    f.n_chunks = (int)n_chunks;
+    f.n_chunks = (int)ceil_div(T, L.fwd_tile);
     f.ctrl = reinterpret_cast<uint32_t*>(base);
     f.status = reinterpret_cast<uint32_t*>(base + L.fwd.off_status);
     f.recs = base + L.fwd.off_recs;
     f.dump_a = planes;
     f.dump_b = planes + ps;
     f.dump_p = planes + 2 * ps;
-    if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), wkv::kBwdTile, stream) != hipSuccess)
+    if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), L.fwd_tile, stream) != hipSuccess)
         return WKV_EHIP;
 
     // 2-5. reverse scan and gradients
@@ -294,7 +298,7 @@ wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.part = planes + 3 * ps;
     a.plane = (long)ps;
     a.ctrl = f.ctrl;
-    a.status = f.status;
+    a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
     a.rrecs = base + L.off_rrecs;
     a.B = (int)B;
     a.T = (int)T;

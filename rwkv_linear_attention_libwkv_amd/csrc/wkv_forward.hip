@@ -510,24 +510,30 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
         sh.ca[lane] = prefix.a;
         sh.cb[lane] = prefix.b;
         sh.cp[lane] = prefix.p;
-        if (args.dump_a) {  // the state entering this tile, for the backward pass
-            const size_t di = ((size_t)ci * args.n_groups + g) * 64 + (c & 63);
-            args.dump_a[di] = prefix.a;
-            args.dump_b[di] = prefix.b;
-            args.dump_p[di] = (float)prefix.p;
-        }
         if constexpr (FAST) {
             asm volatile("" ::: "memory");
             chunk.unstash(sh.stash, lane);
         }
     }
     __syncthreads();
-    if (nv == 0 || args.y == nullptr) return;  // no y: the states were all that was asked
+    if (nv == 0) return;
 
     // ---- outputs of this wave from the state entering its tokens ----
     const Carry tile_in{sh.ca[lane], sh.cb[lane], sh.cp[lane]};
     const Carry before{sh.a[wid][lane], sh.b[wid][lane], sh.p[wid][lane]};
     const Carry cin = normalize(combine(tile_in, before, (double)(wid * L) * w2_of(ch)));
+    if (args.dump_a) {
+        // the state entering every kBwdTile-th time step, for the backward scan
+        const int t0 = t_tile + wid * L;
+        if (t0 % kBwdTile == 0) {
+            const Carry r = rec_form(cin);
+            const size_t di = ((size_t)(t0 / kBwdTile) * args.n_groups + g) * 64 + (c & 63);
+            args.dump_a[di] = r.a;
+            args.dump_b[di] = r.b;
+            args.dump_p[di] = (float)r.p;
+        }
+        if (args.y == nullptr) return;  // no y: the states were all that was asked
+    }
     if (FAST && __all(cin.p - (double)R <= (double)kSpan)) {
         chunk.outputs(ch, cin, R);
         chunk.store(rows, cvalid);

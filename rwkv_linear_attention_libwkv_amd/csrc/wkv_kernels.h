@@ -18,6 +18,9 @@ constexpr int kCtrlWords = 128;  // 512 bytes
 constexpr uint32_t kCtrlEpochMask = 0x3fffffffu;
 constexpr uint32_t kCtrlGiveUpMark = 0x40000000u;
 
+// Time steps per tile of the backward scan.
+constexpr int kBwdTile = 128;
+
 // Arguments of the forward kernels (plain pointers; see include/libwkv.h for meaning).
 struct FwdArgs {
     const float* w;
@@ -33,9 +36,9 @@ struct FwdArgs {
     float* sout_p;
     // chunked algorithm only (workspace carve-up)
     uint32_t* ctrl;  // control block, kCtrlWords words
-    float* dump_a;     // optional [n_chunks][n_groups * 64] state entering each tile (record
-    float* dump_b;     //   form: A = a 2^p, B = b 2^p, p in log2 units); with y null the
-    float* dump_p;     //   kernel writes only these (no outputs)
+    float* dump_a;     // optional [ceil(T / kBwdTile)][n_groups * 64] state entering every
+    float* dump_b;     //   kBwdTile-th time step (record form: A = a 2^p, B = b 2^p, p in
+    float* dump_p;     //   log2 units; needs tile >= kBwdTile); y may then be null (no outputs)
     uint32_t* status;  // [n_groups][n_chunks] status hints
     void* recs;        // [n_chunks][n_groups][2][3][64] tagged 64-bit words
     int B, T, C;
@@ -58,9 +61,8 @@ hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, 
                              float* ob, float* op, long n, hipStream_t s);
 
 // Backward (gradients of sum(gy * y)): a chained scan backwards in time over tiles of
-// kBwdTile tokens x 64 channels that line up with the forward tiles whose entering states
-// the forward kernel dumped.
-constexpr int kBwdTile = 128;
+// kBwdTile tokens x 64 channels, started from the forward states the forward kernel dumped
+// at those tiles' starts.
 struct BwdArgs {
     const float* w;
     const float* u;
