@@ -194,6 +194,34 @@ wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Training pair that skips the backward's forward scan.  wkv_forward_save is
+ * wkv_forward_ex with the chunked algorithm at the default chunk length (its
+ * workspace: wkv_forward_workspace_bytes(B, T, C, dt, WKV_ALGO_CHUNKED, 0))
+ * that also writes, into `saved`, the state entering every 128th time step of
+ * every lane: wkv_saved_states_bytes(B, T, C) bytes of device memory (about
+ * 0.1 byte per element of k; opaque; (size_t)-1 for invalid sizes, 0 for
+ * empty problems).  wkv_backward_saved then gives what wkv_backward gives for
+ * the same w, u, k, v, gy, reading those states instead of recomputing them;
+ * its workspace is wkv_backward_workspace_bytes(...).  The gradients are
+ * bitwise those of wkv_backward.  A `saved` NULL or smaller than the query
+ * gives WKV_EINVAL.
+ */
+size_t wkv_saved_states_bytes(int64_t B, int64_t T, int64_t C);
+
+wkv_status wkv_forward_save(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                            const float* w, const float* u,
+                            const void* k, const void* v, void* y,
+                            float* saved, size_t saved_bytes,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+wkv_status wkv_backward_saved(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                              const float* w, const float* u,
+                              const void* k, const void* v, const void* gy,
+                              const float* saved, size_t saved_bytes,
+                              void* gk, void* gv, float* gw, float* gu,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * One RNN-mode decoding step for N sequences x G layer slots x C channels
  * (section "RNN-유사추론" equation, and steps 4 and 7 of its decoding list:
  * update the WKV state, then store it for the next token).

@@ -75,11 +75,17 @@ bool sizes_ok(int64_t B, int64_t T, int64_t C) {
     return true;
 }
 
+// States saved for the backward: 3 float32 planes (a, b, p in record form) of
+// [ceil(T / kBwdTile)][n_lanes], each plane padded to kAlign bytes.
+size_t saved_plane_bytes(int64_t B, int64_t T, int64_t C) {
+    return align_up((size_t)ceil_div(T, wkv::kBwdTile) * (size_t)(B * ceil_div(C, 64) * 64) * 4, kAlign);
+}
+
 wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w,
                         const float* u, const void* k, const void* v, void* y,
                         const float* sia, const float* sib, const float* sip, float* soa,
                         float* sob, float* sop, void* ws, size_t ws_bytes, wkv_algo algo,
-                        int64_t chunk_len, hipStream_t stream) {
+                        int64_t chunk_len, hipStream_t stream, float* saved = nullptr) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
     if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return WKV_EINVAL;
@@ -121,6 +127,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     }
 
     const int tile = chunk_len ? (int)chunk_len : default_tile(B, T, C);
+    if (saved && tile < wkv::kBwdTile) return WKV_EINVAL;
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
     const int io = chunk_io(dt, C, k, v, y);
@@ -134,6 +141,12 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.ctrl = reinterpret_cast<uint32_t*>(base);
     a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
     a.recs = base + L.off_recs;
+    if (saved) {
+        const size_t ps = saved_plane_bytes(B, T, C) / 4;
+        a.dump_a = saved;
+        a.dump_b = saved + ps;
+        a.dump_p = saved + 2 * ps;
+    }
     return wkv::launch_fwd_chunked(a, io, tile, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
@@ -141,9 +154,9 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
 // (its control block first, so the forward diagnostics read it too; the backward scan
 // reuses the control block after the forward scan), the backward scan's status words and
 // records (two carries of five tagged 64-bit words per kBwdTile tile and channel), then
-// float32 planes of [n_chunks][n_lanes]: 3 for the forward states entering each tile,
-// 2 for partial sums.
-constexpr int kBwdPlanes = 3 + 2;
+// float32 planes of [n_chunks][n_lanes]: 2 for partial sums, 3 for the forward states
+// entering each tile (unused when the caller passes saved states).
+constexpr int kBwdPlanes = 2 + 3;
 
 struct BwdLayout {
     int fwd_tile;
@@ -164,6 +177,96 @@ BwdLayout backward_layout(int64_t B, int64_t T, int64_t C) {
     L.plane_bytes = align_up((size_t)n_chunks * (size_t)n_lanes * 4, kAlign);
     L.total = L.off_planes + kBwdPlanes * L.plane_bytes;
     return L;
+}
+
+// saved: states from wkv_forward_save, or null to recompute them with a forward scan.
+wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                         const void* k, const void* v, const void* gy, const float* saved, size_t saved_bytes,
+                         void* gk, void* gv, float* gw, float* gu, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (!sizes_ok(B, T, C)) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (B == 0 || C == 0) return WKV_OK;
+    if (!gw || !gu) return WKV_EINVAL;
+    if (T == 0) {  // no token: every gradient of w and u is zero
+        return wkv::launch_zero_words(gw, (size_t)(B * C), stream) == hipSuccess &&
+                       wkv::launch_zero_words(gu, (size_t)(B * C), stream) == hipSuccess
+                   ? WKV_OK
+                   : WKV_EHIP;
+    }
+    if (!w || !u || !k || !v || !gy || !gk || !gv) return WKV_EINVAL;
+    const size_t sps = saved_plane_bytes(B, T, C);
+    if (saved && saved_bytes < 3 * sps) return WKV_EINVAL;
+    const BwdLayout L = backward_layout(B, T, C);
+    if (!ws || ws_bytes < L.total) return WKV_EWORKSPACE;
+    const int groups_per_row = (int)ceil_div(C, 64);
+    const int64_t n_groups = B * groups_per_row;
+    const int64_t n_chunks = ceil_div(T, wkv::kBwdTile);
+    if (n_groups * n_chunks > INT_MAX) return WKV_EINVAL;
+    // ws is at least 4-byte aligned by the caller's allocator; the layout aligns every part
+    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    float* planes = reinterpret_cast<float*>(base + L.off_planes);
+    const size_t ps = L.plane_bytes / 4;  // plane stride in floats
+
+    // 1. forward states entering every tile (no outputs), unless the caller saved them
+    const float* fw = saved;
+    size_t fps = sps / 4;
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(base);
+    if (!saved) {
+        wkv::FwdArgs f{};
+        f.w = w;
+        f.u = u;
+        f.k = k;
+        f.v = v;
+        f.y = nullptr;
+        f.B = (int)B;
+        f.T = (int)T;
+        f.C = (int)C;
+        f.groups_per_row = groups_per_row;
+        f.n_groups = (int)n_groups;
+        f.n_chunks = (int)ceil_div(T, L.fwd_tile);
+        f.ctrl = ctrl;
+        f.status = reinterpret_cast<uint32_t*>(base + L.fwd.off_status);
+        f.recs = base + L.fwd.off_recs;
+        f.dump_a = planes + 2 * ps;
+        f.dump_b = planes + 3 * ps;
+        f.dump_p = planes + 4 * ps;
+        if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), L.fwd_tile, stream) != hipSuccess)
+            return WKV_EHIP;
+        fw = planes + 2 * ps;
+        fps = ps;
+    }
+
+    // 2. the backward scan and the partial-sum reduction
+    wkv::BwdArgs a{};
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.gy = gy;
+    a.gk = gk;
+    a.gv = gv;
+    a.gw = gw;
+    a.gu = gu;
+    a.fw_a = fw;
+    a.fw_b = fw + fps;
+    a.fw_p = fw + 2 * fps;
+    a.part = planes;
+    a.plane = (long)ps;
+    a.ctrl = ctrl;
+    a.inherit_give_up = saved == nullptr;
+    a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
+    a.rrecs = base + L.off_rrecs;
+    a.B = (int)B;
+    a.T = (int)T;
+    a.C = (int)C;
+    a.groups_per_row = groups_per_row;
+    a.n_groups = (int)n_groups;
+    a.n_chunks = (int)n_chunks;
+    a.n_lanes = (long)(n_groups * 64);
+    int io = chunk_io(dt, C, k, v, gy);
+    if (io == wkv::kIoBf16Pair && !(aligned(gk, 4) && aligned(gv, 4))) io = wkv::kIoBf16;
+    return wkv::launch_bwd(a, io, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 }  // namespace
@@ -237,79 +340,32 @@ size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype d
 wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
                         const void* k, const void* v, const void* gy, void* gk, void* gv, float* gw,
                         float* gu, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return backward_impl(B, T, C, dt, w, u, k, v, gy, nullptr, 0, gk, gv, gw, gu, ws, ws_bytes, stream);
+}
+
+size_t wkv_saved_states_bytes(int64_t B, int64_t T, int64_t C) {
+    if (!sizes_ok(B, T, C)) return (size_t)-1;
+    if (B == 0 || T == 0 || C == 0) return 0;
+    return 3 * saved_plane_bytes(B, T, C);
+}
+
+wkv_status wkv_forward_save(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                            const void* k, const void* v, void* y, float* saved, size_t saved_bytes, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
-    if (B == 0 || C == 0) return WKV_OK;
-    if (!gw || !gu) return WKV_EINVAL;
-    if (T == 0) {  // no token: every gradient of w and u is zero
-        return wkv::launch_zero_words(gw, (size_t)(B * C), stream) == hipSuccess &&
-                       wkv::launch_zero_words(gu, (size_t)(B * C), stream) == hipSuccess
-                   ? WKV_OK
-                   : WKV_EHIP;
-    }
-    if (!w || !u || !k || !v || !gy || !gk || !gv) return WKV_EINVAL;
-    const BwdLayout L = backward_layout(B, T, C);
-    if (!ws || ws_bytes < L.total) return WKV_EWORKSPACE;
-    const int groups_per_row = (int)ceil_div(C, 64);
-    const int64_t n_groups = B * groups_per_row;
-    const int64_t n_chunks = ceil_div(T, wkv::kBwdTile);
-    if (n_groups * n_chunks > INT_MAX) return WKV_EINVAL;
-    // ws is at least 4-byte aligned by the caller's allocator; the layout aligns every part
-    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
-    float* planes = reinterpret_cast<float*>(base + L.off_planes);
-    const size_t ps = L.plane_bytes / 4;  // plane stride in floats (>= plane)
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    if (!saved || saved_bytes < 3 * saved_plane_bytes(B, T, C)) return WKV_EINVAL;
+    return forward_impl(B, T, C, dt, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, ws,
+                        ws_bytes, WKV_ALGO_CHUNKED, 0, stream, saved);
+}
 
-    // 1. forward states entering every tile (no outputs)
-    wkv::FwdArgs f{};
-    f.w = w;
-    f.u = u;
-    f.k = k;
-    f.v = v;
-    f.y = nullptr;
-    f.B = (int)B;
-    f.T = (int)T;
-    f.C = (int)C;
-    f.groups_per_row = groups_per_row;
-    f.n_groups = (int)n_groups;
-    f.n_chunks = (int)ceil_div(T, L.fwd_tile);
-    f.ctrl = reinterpret_cast<uint32_t*>(base);
-    f.status = reinterpret_cast<uint32_t*>(base + L.fwd.off_status);
-    f.recs = base + L.fwd.off_recs;
-    f.dump_a = planes;
-    f.dump_b = planes + ps;
-    f.dump_p = planes + 2 * ps;
-    if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), L.fwd_tile, stream) != hipSuccess)
-        return WKV_EHIP;
-
-    // 2-5. reverse scan and gradients
-    wkv::BwdArgs a{};
-    a.w = w;
-    a.u = u;
-    a.k = k;
-    a.v = v;
-    a.gy = gy;
-    a.gk = gk;
-    a.gv = gv;
-    a.gw = gw;
-    a.gu = gu;
-    a.fw_a = planes;
-    a.fw_b = planes + ps;
-    a.fw_p = planes + 2 * ps;
-    a.part = planes + 3 * ps;
-    a.plane = (long)ps;
-    a.ctrl = f.ctrl;
-    a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
-    a.rrecs = base + L.off_rrecs;
-    a.B = (int)B;
-    a.T = (int)T;
-    a.C = (int)C;
-    a.groups_per_row = groups_per_row;
-    a.n_groups = (int)n_groups;
-    a.n_chunks = (int)n_chunks;
-    a.n_lanes = (long)(n_groups * 64);
-    int io = chunk_io(dt, C, k, v, gy);
-    if (io == wkv::kIoBf16Pair && !(aligned(gk, 4) && aligned(gv, 4))) io = wkv::kIoBf16;
-    return wkv::launch_bwd(a, io, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+wkv_status wkv_backward_saved(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                              const void* k, const void* v, const void* gy, const float* saved,
+                              size_t saved_bytes, void* gk, void* gv, float* gw, float* gu, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (B > 0 && T > 0 && C > 0 && !saved) return WKV_EINVAL;
+    return backward_impl(B, T, C, dt, w, u, k, v, gy, saved, saved_bytes, gk, gv, gw, gu, ws, ws_bytes, stream);
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

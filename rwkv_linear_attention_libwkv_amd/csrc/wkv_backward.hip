@@ -566,7 +566,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
         args.part[plane + ti] = su;
     }
     // ---- launch bookkeeping (a give-up of the forward scan before is carried over) ----
-    if (threadIdx.x == 0) finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, true);
+    if (threadIdx.x == 0)
+        finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, args.inherit_give_up);
 }
 
 // dL/dw and dL/du per lane: the tiles' partials summed in a fixed order.  Block: 64 lanes

@@ -81,6 +81,7 @@ struct BwdArgs {
     uint32_t* ctrl;     // control block (shared with the forward scan, which runs first)
     uint32_t* status;   // [n_groups][n_chunks] status hints
     void* rrecs;        // [n_chunks][n_groups][2][5][64] tagged 64-bit words
+    bool inherit_give_up;  // a forward scan ran just before on the same control block
     int B, T, C;
     int groups_per_row, n_groups, n_chunks;
     long n_lanes;       // n_groups * 64

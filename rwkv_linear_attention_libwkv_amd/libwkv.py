@@ -31,6 +31,9 @@ EXPORTS = (
     "wkv_step",
     "wkv_backward_workspace_bytes",
     "wkv_backward",
+    "wkv_saved_states_bytes",
+    "wkv_forward_save",
+    "wkv_backward_saved",
     "wkv_status_string",
 )
 
@@ -71,6 +74,12 @@ def _load() -> ctypes.CDLL:
     lib.wkv_backward_workspace_bytes.restype = sz
     lib.wkv_backward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wkv_backward.restype = i32
+    lib.wkv_saved_states_bytes.argtypes = [i64, i64, i64]
+    lib.wkv_saved_states_bytes.restype = sz
+    lib.wkv_forward_save.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.wkv_forward_save.restype = i32
+    lib.wkv_backward_saved.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
+    lib.wkv_backward_saved.restype = i32
     lib.wkv_status_string.argtypes = [i32]
     lib.wkv_status_string.restype = ctypes.c_char_p
     return lib
@@ -229,11 +238,45 @@ def new_backward_workspace(B: int, T: int, C: int, dtype=torch.float32, device="
     return wkv_forward_workspace_init(ws)
 
 
-def wkv_backward(w, u, k, v, gy, *, gk=None, gv=None, gw=None, gu=None, workspace=None, stream=None):
+def wkv_saved_states_bytes(B: int, T: int, C: int) -> int:
+    n = lib.wkv_saved_states_bytes(B, T, C)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for the saved-state query")
+    return int(n)
+
+
+def wkv_forward_save(w, u, k, v, *, y=None, saved=None, workspace=None, stream=None):
+    """y = WKV(w, u, k, v) plus the states wkv_backward_saved needs: returns (y, saved).
+
+    ``saved`` is an opaque uint8 device tensor of wkv_saved_states_bytes(B, T, C) bytes.
+    """
+    _need(k.dim() == 3 and v.shape == k.shape and k.dtype == v.dtype, "k and v must be [B, T, C] of one dtype")
+    _need(k.is_contiguous() and v.is_contiguous() and k.is_cuda, "k and v must be contiguous GPU tensors")
+    B, T, C = k.shape
+    _need(w.numel() == C and u.numel() == C and w.dtype == torch.float32 and u.dtype == torch.float32,
+          "w and u must be float32 with C entries")
+    y = torch.empty_like(k) if y is None else y
+    _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    nbytes = wkv_saved_states_bytes(B, T, C)
+    if saved is None:
+        saved = torch.empty(max(4, nbytes), dtype=torch.uint8, device=k.device)
+    _need(saved.is_cuda and saved.is_contiguous(), "bad saved buffer")
+    if workspace is None:
+        workspace = new_workspace(B, T, C, k.dtype, "chunked", 0, device=k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wkv_forward_save(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                _ptr(saved), saved.numel() * saved.element_size(), _ptr(workspace), ws_bytes,
+                                _stream(stream)), "wkv_forward_save")
+    return y, saved
+
+
+def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=None, workspace=None,
+                 stream=None):
     """Gradients of sum(gy * WKV(w, u, k, v)): returns (gw, gu, gk, gv).
 
     k, v, gy: [B, T, C] (float32 or bfloat16, on the GPU); gk, gv have their dtype;
     gw, gu are float32 [B, C] per-lane gradients (sum over B for the [C] parameters).
+    With ``saved`` (from wkv_forward_save) calls wkv_backward_saved, else wkv_backward.
     """
     _need(k.dim() == 3 and v.shape == k.shape and gy.shape == k.shape, "k, v and gy must be [B, T, C]")
     _need(k.is_cuda and v.is_cuda and gy.is_cuda and w.is_cuda and u.is_cuda, "all tensors must be on the GPU")
@@ -254,9 +297,16 @@ def wkv_backward(w, u, k, v, gy, *, gk=None, gv=None, gw=None, gu=None, workspac
     if workspace is None:
         workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.wkv_backward(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
-                            _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(workspace), ws_bytes, _stream(stream)),
-           "wkv_backward")
+    if saved is None:
+        _check(lib.wkv_backward(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                                _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(workspace), ws_bytes,
+                                _stream(stream)), "wkv_backward")
+    else:
+        _need(saved.is_cuda and saved.is_contiguous(), "bad saved buffer")
+        _check(lib.wkv_backward_saved(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                      _ptr(gy), _ptr(saved), saved.numel() * saved.element_size(), _ptr(gk),
+                                      _ptr(gv), _ptr(gw), _ptr(gu), _ptr(workspace), ws_bytes, _stream(stream)),
+               "wkv_backward_saved")
     return gw, gu, gk, gv
 
 
@@ -291,4 +341,5 @@ def workspace_epoch(workspace, stream=None) -> int:
 forward = wkv_forward
 step = wkv_step
 backward = wkv_backward
+forward_save = wkv_forward_save
 workspace_bytes = wkv_forward_workspace_bytes

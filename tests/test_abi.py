@@ -160,6 +160,25 @@ def test_backward_workspace_query():
     assert a > lib.wkv_forward_workspace_bytes(8, 8192, 2048, F32, 2, 0)
 
 
+def test_saved_state_entry_points_argument_checks():
+    q = lib.wkv_saved_states_bytes
+    assert q(-1, 4, 4) == ctypes.c_size_t(-1).value
+    assert q(0, 4, 4) == 0 and q(4, 0, 4) == 0
+    need = q(2, 300, 64)
+    assert need >= 3 * 3 * 2 * 64 * 4  # three planes of ceil(300 / 128) x 128 lanes
+    fs = lib.wkv_forward_save
+    assert fs(2, 300, 64, F32, P, P, P, P, P, NULL, 0, P, 1 << 30, None) == EINVAL
+    assert fs(2, 300, 64, F32, P, P, P, P, P, P, need - 1, P, 1 << 30, None) == EINVAL
+    assert fs(2, 300, 64, 9, P, P, P, P, P, P, need, P, 1 << 30, None) == EDTYPE
+    assert fs(2, 300, 64, F32, P, P, P, P, P, P, need, NULL, 0, None) == EWS
+    assert fs(0, 300, 64, F32, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, 0, None) == OK
+    bs = lib.wkv_backward_saved
+    wsb = lib.wkv_backward_workspace_bytes(2, 300, 64, F32)
+    assert bs(2, 300, 64, F32, P, P, P, P, P, NULL, 0, P, P, P, P, P, wsb, None) == EINVAL
+    assert bs(2, 300, 64, F32, P, P, P, P, P, P, need - 1, P, P, P, P, P, wsb, None) == EINVAL
+    assert bs(2, 300, 64, F32, P, P, P, P, P, P, need, P, P, P, P, P, wsb - 1, None) == EWS
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import importlib
 

@@ -218,3 +218,23 @@ def test_bf16_row_pairs_match_two_byte_lanes():
     torch.cuda.synchronize()
     for name, a, b in zip(NAMES, pair, lanes):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("dtype,B,T,C", [("f32", 2, 1000, 130), ("f32", 1, 100, 64), ("bf16", 2, 700, 192),
+                                         ("bf16", 1, 300, 67)])
+def test_saved_states_give_the_same_gradients(dtype, B, T, C):
+    """wkv_forward_save gives wkv_forward's chunked y; wkv_backward_saved gives wkv_backward's
+    gradients bit for bit; the saved pair needs one scan per call on its workspace."""
+    inp = grad_inputs(B, T, C, seed=41 + T, dtype=dtype, k_std=1.5)
+    dev = to_device(inp)
+    y_ref = libwkv.wkv_forward(dev["w"], dev["u"], dev["k"], dev["v"], algo="chunked")
+    y, saved = libwkv.wkv_forward_save(dev["w"], dev["u"], dev["k"], dev["v"])
+    ref = libwkv.wkv_backward(dev["w"], dev["u"], dev["k"], dev["v"], dev["gy"])
+    ws = libwkv.new_backward_workspace(B, T, C, dev["k"].dtype)
+    got = libwkv.wkv_backward(dev["w"], dev["u"], dev["k"], dev["v"], dev["gy"], saved=saved, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    for name, a, b in zip(NAMES, got, ref):
+        assert torch.equal(a, b), name
+    gave_up, epoch = libwkv.workspace_query(ws)
+    assert gave_up == 0 and epoch == 1
