@@ -27,19 +27,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("wkv_forward.hip", "wkv_step.hip", "wkv_backward.hip", "wkv_rows.h", "wkv_device.h",
-                  "wkv_kernels.h", "libwkv_api.cpp")
+# sources of the forward kernel and its launch path (the committed counter runs are valid
+# for the kernel built from exactly these)
+KERNEL_SOURCES = ("wkv_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h",
+                  "libwkv_api.cpp")
+BACKWARD_SOURCES = KERNEL_SOURCES + ("wkv_backward.hip",)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "rwkv_linear_attention_libwkv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -47,7 +50,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(sources):
         return None
     return entry.get("bytes_per_launch")
 
@@ -148,6 +151,17 @@ def backward_case(spec, steps, warmup):
 
     wall, per_call = time_launches(fn, steps, warmup)
     assert libwkv.lookback_error(ws) == 0, "look-back gave up"
+    # the training pair: forward that saves the scan's states, backward that starts from them
+    y = torch.empty_like(k)
+    fws = libwkv.new_workspace(spec.B, spec.T, spec.C, dt, "chunked", 0)
+    _, saved = libwkv.wkv_forward_save(w, u, k, v, y=y, workspace=fws)
+
+    def train():
+        libwkv.wkv_forward_save(w, u, k, v, y=y, saved=saved, workspace=fws)
+        libwkv.wkv_backward(w, u, k, v, gy, saved=saved, gk=gk, gv=gv, gw=gw, gu=gu, workspace=ws)
+
+    _, per_train = time_launches(train, steps, warmup)
+    assert libwkv.lookback_error(ws) == 0 and libwkv.lookback_error(fws) == 0, "look-back gave up"
     elt = 4 if spec.dtype == "f32" else 2
     bytes_per_launch = 5 * elt * spec.elements + 8 * spec.B * spec.C  # read k, v, gy; write gk, gv, gw, gu
     out = {
@@ -157,8 +171,12 @@ def backward_case(spec, steps, warmup):
         "elements_per_s": spec.elements / per_call,
         "algorithmic_bytes_per_launch": bytes_per_launch,
         "achieved_GBps": bytes_per_launch / per_call / 1e9,
+        "scan_kernel_traffic_bytes": measured_traffic(spec.name.replace("wkv_fwd", "wkv_bwd"), BACKWARD_SOURCES),
+        "train_pair_s": per_train,
+        "train_pair_note": "wkv_forward_save + wkv_backward_saved (y, then all four gradients)",
+        "train_pair_algorithmic_GBps": (bytes_per_launch + 3 * elt * spec.elements) / per_train / 1e9,
     }
-    del k, v, gy, gk, gv, ws
+    del k, v, gy, gk, gv, ws, y, fws, saved
     torch.cuda.empty_cache()
     return out
 
@@ -299,7 +317,8 @@ def main():
             r = backward_case(s, max(5, args.steps // 2), 2)
             others.append(r)
             print(f"# {r['workload']}: {r['per_launch_s'] * 1e6:.1f} us/call, {r['achieved_GBps']:.0f} GB/s "
-                  f"(algorithmic bytes)", file=sys.stderr, flush=True)
+                  f"(algorithmic bytes); forward_save + backward_saved {r['train_pair_s'] * 1e6:.1f} us, "
+                  f"{r['train_pair_algorithmic_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
         r = step_case(workloads.STEP_DECODE, args.steps, 1)
         others.append(r)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "
