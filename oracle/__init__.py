@@ -12,6 +12,9 @@ It evaluates what the pages define, slowly and plainly:
 * ``wkv_step_ref``    -- one RNN-mode step from a given (a, b, p) state
 * ``wkv_mp``          -- the defining sums at 50 significant digits (mpmath)
 * ``wkv_backward_direct`` -- gradients of the defining sums, O(T^2)
+* ``token_shift``, ``token_shift_backward`` -- the time-mixing token shift (lerp of
+  x_t and x_{t-1}) and its gradients
+* ``wkv_gated``, ``wkv_gated_backward`` -- the output gate sigmoid(r) * wkv and its gradients
 * ``scaled_error``    -- the scale-normalised error used as the parity gate
 
 Citations name the page ("Reinventing RNNs for the Transformer Era: RWKV",
@@ -29,3 +32,4 @@ from .wkv_oracle import (  # noqa: F401
 )
 from .wkv_mp import wkv_mp  # noqa: F401
 from .wkv_grad import wkv_backward_direct  # noqa: F401
+from .wkv_mix import sigmoid, token_shift, token_shift_backward, wkv_gated, wkv_gated_backward  # noqa: F401
