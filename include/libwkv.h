@@ -222,6 +222,55 @@ wkv_status wkv_backward_saved(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The time-mixing block around WKV (page "Reinventing RNNs for the Transformer
+ * Era: RWKV", sections "토큰 변환" and "출력 게이팅"); the dense projections
+ * between them (W_r, W_k, W_v before, W_o after) are not part of this library.
+ *
+ * wkv_token_shift: the inputs of the R, K, V projections, a per-channel linear
+ * interpolation between the current and the previous time step:
+ *   out[m, b, t, c] = mu[m, c] x[b, t, c] + (1 - mu[m, c]) x[b, t-1, c],
+ * for m < M (1 <= M <= 4, else WKV_EINVAL), x[b, -1, c] = x_prev[b, c] (the last
+ * token of the previous call when a sequence continues) or 0 when x_prev is
+ * NULL.  x: [B, T, C] dtype dt; x_prev: [B, C] dtype dt or NULL; mu: [M, C]
+ * float32; out: [M, B, T, C] dtype dt, must not alias x.
+ */
+wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                           const void* x, const void* x_prev, const float* mu,
+                           int64_t M, void* out, hipStream_t stream);
+
+/*
+ * wkv_forward_gated: z = sigmoid(r) * WKV(w, u, k, v) elementwise, the gated
+ * value the output projection W_o consumes, with the gate fused into the
+ * output stores (one pass; no WKV intermediate in memory).  r and z are
+ * [B, T, C] of dtype dt.  With `saved` non-NULL this is wkv_forward_save with
+ * the gate (chunked algorithm, the states kept for the backward; workspace of
+ * wkv_forward_workspace_bytes(..., WKV_ALGO_CHUNKED, 0)); with `saved` NULL the
+ * algorithm is AUTO (workspace of wkv_forward_workspace_bytes(..., WKV_ALGO_AUTO,
+ * 0)).  bfloat16 z: the float32 product rounded to nearest even, except with
+ * bf16 row pairs in the chunked algorithm (even C, 4-byte aligned arrays),
+ * where the gate multiplies the bf16-rounded WKV (within 1.5 units in the last
+ * place instead of 0.5).
+ *
+ * wkv_backward_gated: given gz = dL/dz, all of wkv_backward's gradients (for
+ * dL/dy = gz * sigmoid(r)) and gr = dL/dr = gz * WKV * sigmoid(r) *
+ * sigmoid(-r) ([B, T, C], dtype dt), in the same single backward scan.
+ * `saved` as in wkv_backward_saved, or NULL to recompute the forward states;
+ * workspace of wkv_backward_workspace_bytes(...).
+ */
+wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                             const float* w, const float* u,
+                             const void* k, const void* v, const void* r, void* z,
+                             float* saved, size_t saved_bytes,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                              const float* w, const float* u,
+                              const void* k, const void* v, const void* r, const void* gz,
+                              const float* saved, size_t saved_bytes,
+                              void* gk, void* gv, void* gr, float* gw, float* gu,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * One RNN-mode decoding step for N sequences x G layer slots x C channels
  * (section "RNN-유사추론" equation, and steps 4 and 7 of its decoding list:
  * update the WKV state, then store it for the next token).

@@ -85,7 +85,8 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
                         const float* u, const void* k, const void* v, void* y,
                         const float* sia, const float* sib, const float* sip, float* soa,
                         float* sob, float* sop, void* ws, size_t ws_bytes, wkv_algo algo,
-                        int64_t chunk_len, hipStream_t stream, float* saved = nullptr) {
+                        int64_t chunk_len, hipStream_t stream, float* saved = nullptr,
+                        const void* r = nullptr) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
     if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return WKV_EINVAL;
@@ -109,6 +110,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.k = k;
     a.v = v;
     a.y = y;
+    a.r = r;
     a.sin_a = sia;
     a.sin_b = sib;
     a.sin_p = sip;
@@ -130,7 +132,8 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     if (saved && tile < wkv::kBwdTile) return WKV_EINVAL;
     const size_t need = chunked_bytes_bound(B, T, C, tile);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
-    const int io = chunk_io(dt, C, k, v, y);
+    int io = chunk_io(dt, C, k, v, y);
+    if (io == wkv::kIoBf16Pair && r && !aligned(r, 4)) io = wkv::kIoBf16;
     a.groups_per_row = (int)ceil_div(C, 64);
     a.n_groups = (int)(B * a.groups_per_row);
     a.n_chunks = (int)ceil_div(T, tile);
@@ -180,10 +183,11 @@ BwdLayout backward_layout(int64_t B, int64_t T, int64_t C) {
 }
 
 // saved: states from wkv_forward_save, or null to recompute them with a forward scan.
+// r, gr: the output gate and its gradient (both null without a gate; gy is then dL/dz).
 wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
                          const void* k, const void* v, const void* gy, const float* saved, size_t saved_bytes,
                          void* gk, void* gv, float* gw, float* gu, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void* r = nullptr, void* gr = nullptr) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
     if (B == 0 || C == 0) return WKV_OK;
@@ -244,6 +248,8 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const fl
     a.k = k;
     a.v = v;
     a.gy = gy;
+    a.r = r;
+    a.gr = gr;
     a.gk = gk;
     a.gv = gv;
     a.gw = gw;
@@ -266,6 +272,7 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const fl
     a.n_lanes = (long)(n_groups * 64);
     int io = chunk_io(dt, C, k, v, gy);
     if (io == wkv::kIoBf16Pair && !(aligned(gk, 4) && aligned(gv, 4))) io = wkv::kIoBf16;
+    if (io == wkv::kIoBf16Pair && r && !(aligned(r, 4) && aligned(gr, 4))) io = wkv::kIoBf16;
     return wkv::launch_bwd(a, io, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
@@ -366,6 +373,51 @@ wkv_status wkv_backward_saved(int64_t B, int64_t T, int64_t C, wkv_dtype dt, con
                               size_t ws_bytes, hipStream_t stream) {
     if (B > 0 && T > 0 && C > 0 && !saved) return WKV_EINVAL;
     return backward_impl(B, T, C, dt, w, u, k, v, gy, saved, saved_bytes, gk, gv, gw, gu, ws, ws_bytes, stream);
+}
+
+wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                             const void* k, const void* v, const void* r, void* z, float* saved,
+                             size_t saved_bytes, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!sizes_ok(B, T, C)) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    if (!r) return WKV_EINVAL;
+    if (saved && saved_bytes < 3 * saved_plane_bytes(B, T, C)) return WKV_EINVAL;
+    return forward_impl(B, T, C, dt, w, u, k, v, z, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, ws,
+                        ws_bytes, saved ? WKV_ALGO_CHUNKED : WKV_ALGO_AUTO, 0, stream, saved, r);
+}
+
+wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
+                              const void* k, const void* v, const void* r, const void* gz, const float* saved,
+                              size_t saved_bytes, void* gk, void* gv, void* gr, float* gw, float* gu, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (B > 0 && T > 0 && C > 0 && (!r || !gr)) {
+        if (!sizes_ok(B, T, C)) return WKV_EINVAL;
+        return dtype_ok(dt) ? WKV_EINVAL : WKV_EDTYPE;
+    }
+    return backward_impl(B, T, C, dt, w, u, k, v, gz, saved, saved_bytes, gk, gv, gw, gu, ws, ws_bytes, stream, r,
+                         gr);
+}
+
+wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const void* x, const void* x_prev,
+                           const float* mu, int64_t M, void* out, hipStream_t stream) {
+    if (!sizes_ok(B, T, C) || M < 1 || M > wkv::kShiftMaxM) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    if (!x || !mu || !out) return WKV_EINVAL;
+    if (B * T > INT_MAX || B * T * C > (int64_t)1 << 40) return WKV_EINVAL;
+    const size_t vec = dt == WKV_F32 ? 4 : 8;
+    const bool vector = C % (int64_t)vec == 0 && aligned(x, 16) && aligned(out, 16) && (!x_prev || aligned(x_prev, 16));
+    wkv::ShiftArgs a{};
+    a.x = x;
+    a.x_prev = x_prev;
+    a.mu = mu;
+    a.out = out;
+    a.B = (int)B;
+    a.T = (int)T;
+    a.C = (int)C;
+    a.M = (int)M;
+    return wkv::launch_token_shift(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

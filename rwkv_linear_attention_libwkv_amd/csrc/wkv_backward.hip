@@ -144,24 +144,46 @@ struct BwdChunk {
     // dL/dk (in k) and dL/dv (in v) of a full chunk, after backward()
     template <typename IO>
     __device__ __forceinline__ void store_grads(const WaveRows& w, Rsrc gk, Rsrc gv, bool valid) const {
+        store_rows<IO>(w, gk, valid, k);
+        store_rows<IO>(w, gv, valid, v);
+    }
+    // one array of L rows (full chunk), stored in the mode's row format
+    template <typename IO>
+    static __device__ __forceinline__ void store_rows(const WaveRows& w, Rsrc dst, bool valid, const float (&x)[L]) {
         if constexpr (kPair<IO>) {
             const uint32_t sel = pair_sel(w.upper);
 #pragma unroll
             for (int jj = 0; jj < L / 2; ++jj) {
-                const uint32_t wk = pair_exchange(pack_bf16(k[2 * jj], k[2 * jj + 1]), w.partner, sel);
-                const uint32_t wv = pair_exchange(pack_bf16(v[2 * jj], v[2 * jj + 1]), w.partner, sel);
-                if (valid) {
-                    const uint32_t so = (uint32_t)(2 * jj) * w.row_bytes;
-                    __builtin_amdgcn_raw_buffer_store_b32(wk, gk, w.pair_off, so, kStream);
-                    __builtin_amdgcn_raw_buffer_store_b32(wv, gv, w.pair_off, so, kStream);
-                }
+                const uint32_t word = pair_exchange(pack_bf16(x[2 * jj], x[2 * jj + 1]), w.partner, sel);
+                if (valid)
+                    __builtin_amdgcn_raw_buffer_store_b32(word, dst, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
+                                                          kStream);
             }
         } else if (valid) {
 #pragma unroll
-            for (int j = 0; j < L; ++j) {
-                store_elt<IO>(gk, w.lane_off, (uint32_t)j * w.row_bytes, k[j]);
-                store_elt<IO>(gv, w.lane_off, (uint32_t)j * w.row_bytes, v[j]);
+            for (int j = 0; j < L; ++j) store_elt<IO>(dst, w.lane_off, (uint32_t)j * w.row_bytes, x[j]);
+        }
+    }
+    // one array of L rows (full chunk), loaded in the mode's row format
+    template <typename IO>
+    static __device__ __forceinline__ void load_rows(const WaveRows& w, Rsrc src, bool valid, float (&x)[L]) {
+        if constexpr (kPair<IO>) {
+            uint32_t xw[L / 2];
+#pragma unroll
+            for (int jj = 0; jj < L / 2; ++jj)
+                xw[jj] = valid ? __builtin_amdgcn_raw_buffer_load_b32(src, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
+                                                                      kStream)
+                               : 0u;
+            const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+            for (int jj = 0; jj < L / 2; ++jj) {
+                const uint32_t p = pair_exchange(xw[jj], w.partner, sel);
+                x[2 * jj] = bf_lo(p);
+                x[2 * jj + 1] = bf_hi(p);
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < L; ++j) x[j] = valid ? load_elt<IO>(src, w.lane_off, (uint32_t)j * w.row_bytes) : 0.f;
         }
     }
     __device__ __forceinline__ void range(float& kmax, float& kmin) const {
@@ -195,6 +217,24 @@ struct BwdChunk {
             const float inv = rcp(fmaf(ch.eu, x, b));
             y[j] = fmaf(ch.eu, xv, a) * inv;
             g[j] = g[j] * inv;
+            a = fmaf(ch.d, a, xv);
+            b = fmaf(ch.d, b, x);
+        }
+    }
+    // forward() with the output gate z = sigmoid(r) y: g holds dL/dz on entry and becomes
+    // q^ of dL/dy = dL/dz sigmoid(r); r (in sr) is replaced by dL/dr = dL/dy y sigmoid(-r)
+    __device__ __forceinline__ void forward_gated(const Chan& ch, const Carry& cin, float R, float (&sr)[L]) {
+        const float s = ex2((float)(cin.p - (double)R));
+        float a = cin.a * s, b = cin.b * s;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const float x = k[j];
+            const float xv = x * v[j];
+            const float inv = rcp(fmaf(ch.eu, x, b));
+            y[j] = fmaf(ch.eu, xv, a) * inv;
+            const float gyj = g[j] * sigmoid_f(sr[j]);
+            sr[j] = gyj * y[j] * sigmoid_f(-sr[j]);
+            g[j] = gyj * inv;
             a = fmaf(ch.d, a, xv);
             b = fmaf(ch.d, b, x);
         }
@@ -256,9 +296,10 @@ struct BwdChunk {
 // the state entering the wave by walking the earlier tokens of the wave again (O(L^2),
 // read from memory, no per-token arrays), and the reverse sums carry their own float64
 // exponent.  Produces the wave's reverse aggregate (pass 0) or its gradients (pass 1).
-template <typename IO, bool OUT>
+template <typename IO, bool OUT, bool GATE>
 __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, const Rev& rin, const WaveRows& w,
-                                          Rsrc gyr, Rsrc gkr, Rsrc gvr, int nv, bool valid, float& gw, float& gu) {
+                                          Rsrc gyr, Rsrc gkr, Rsrc gvr, Rsrc grr, int nv, bool valid, float& gw,
+                                          float& gu) {
     Rev c = rin;
     const double w2 = w2_of(ch), u2 = u2_of(ch);
 #pragma unroll 1
@@ -275,7 +316,12 @@ __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, cons
         const uint32_t so = (uint32_t)j * w.row_bytes;
         const float kj = valid ? load_elt<IO>(w.k, w.lane_off, so) : 0.f;
         const float vj = valid ? load_elt<IO>(w.v, w.lane_off, so) : 0.f;
-        const float gj = valid ? load_elt<IO>(gyr, w.lane_off, so) : 0.f;
+        float gj = valid ? load_elt<IO>(gyr, w.lane_off, so) : 0.f;
+        float rj = 0.f;
+        if constexpr (GATE) {  // gj is dL/dz: dL/dy = dL/dz sigmoid(r)
+            rj = valid ? load_elt<IO>(w.r, w.lane_off, so) : 0.f;
+            gj *= sigmoid_f(rj);
+        }
         // y_j and q_j = gy_j / D_j = qm 2^qe
         const double k2 = (double)kj * kLog2eD;
         const double uk = u2 + k2;
@@ -285,6 +331,8 @@ __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, cons
         const float inv = rcp(fmaf(e1, st.b, e2));
         const float yj = fmaf(e1, st.a, e2 * vj) * inv;
         const float qm = gj * inv;
+        if constexpr (GATE && !OUT)  // dL/dr, once (in the aggregate pass)
+            if (valid) store_elt<IO>(grr, w.lane_off, so, gj * yj * sigmoid_f(-rj));
         const double qe = -qref;
         if (OUT) {
             const float ek = ex2((float)(k2 + c.r));         // e^{k_j} 2^r
@@ -403,7 +451,7 @@ __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs
 // One tile of the backward scan (see the plan at the top).  Tiles are numbered in the
 // order workgroups start, from the last chunk of the sequence to the first, so every
 // tile this one waits on has started and publishes its aggregate without waiting.
-template <typename IO, int L, int NW>
+template <typename IO, int L, int NW, bool GATE>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     constexpr int TILE = L * NW;
     static_assert(TILE == kBwdTile, "tiles must line up with the dumped forward tiles");
@@ -442,9 +490,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     const Rsrc gyr = make_rsrc(static_cast<const char*>(args.gy) + off);
     const Rsrc gkr = make_rsrc(static_cast<char*>(args.gk) + off);
     const Rsrc gvr = make_rsrc(static_cast<char*>(args.gv) + off);
+    Rsrc grr = gkr;
+    if constexpr (GATE) {
+        rows.r = make_rsrc(static_cast<const char*>(args.r) + off);
+        grr = make_rsrc(static_cast<char*>(args.gr) + off);
+    }
 
     BwdChunk<L> ck;
     ck.template load<IO>(rows, gyr, nv, cvalid);
+    float sr[GATE ? L : 1];  // gate: r rows, then dL/dr
+    if constexpr (GATE) BwdChunk<L>::template load_rows<IO>(rows, rows.r, cvalid && nv == L, sr);
 
     // read after the loads are issued; constant during the launch
     const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
@@ -494,10 +549,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     float gw = 0.f, gu = 0.f;
     Rev ragg;
     if (wave_fast) {
-        ck.forward(ch, fin, R);
+        if constexpr (GATE) {
+            ck.forward_gated(ch, fin, R, sr);
+            BwdChunk<L>::template store_rows<IO>(rows, grr, cvalid, sr);
+        } else {
+            ck.forward(ch, fin, R);
+        }
         ragg = ck.reverse_aggregate(ch, R);
     } else {
-        ragg = exact_wave<IO, false>(ch, fin, empty_rev(), rows, gyr, gkr, gvr, nv, cvalid, gw, gu);
+        ragg = exact_wave<IO, false, GATE>(ch, fin, empty_rev(), rows, gyr, gkr, gvr, grr, nv, cvalid, gw, gu);
     }
     ragg = normalize_rev(ragg);
     sh.g[wid][lane] = ragg.g;
@@ -550,7 +610,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     } else {
         gw = 0.f;
         gu = 0.f;
-        (void)exact_wave<IO, true>(ch, fin, cin, rows, gyr, gkr, gvr, nv, cvalid, gw, gu);
+        (void)exact_wave<IO, true, GATE>(ch, fin, cin, rows, gyr, gkr, gvr, grr, nv, cvalid, gw, gu);
     }
     sh.gw[wid][lane] = gw;
     sh.gu[wid][lane] = gu;
@@ -608,7 +668,10 @@ template <typename IO>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     constexpr int L = 16, NW = kBwdTile / L;
     const unsigned tiles = (unsigned)((long)a.n_groups * a.n_chunks);
-    hipLaunchKernelGGL((bwd_scan_kernel<IO, L, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    if (a.r)
+        hipLaunchKernelGGL((bwd_scan_kernel<IO, L, NW, true>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_scan_kernel<IO, L, NW, false>), dim3(tiles), dim3(64 * NW), 0, s, a);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.n_groups), dim3(64 * kRedSlices), 0, s, a);
     return hipGetLastError();
 }

@@ -151,6 +151,16 @@ struct Chunk {
         }
         return Carry{a, b, (double)R};
     }
+    // outputs() times sigmoid(r): the gate rows are read into v's registers once v is spent
+    __device__ __forceinline__ Carry outputs_gated(const Chan& ch, const Carry& c, float R, const WaveRows& w,
+                                                   bool valid) {
+        const Carry out = outputs(ch, c, R);
+#pragma unroll
+        for (int j = 0; j < L; ++j) v[j] = valid ? load_elt<IO>(w.r, w.lane_off, (uint32_t)j * w.row_bytes) : 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) k[j] *= sigmoid_f(v[j]);
+        return out;
+    }
     __device__ __forceinline__ void store(const WaveRows& w, bool valid) const {
 #pragma unroll
         for (int j = 0; j < L; ++j)
@@ -243,6 +253,28 @@ struct Chunk<Bf16Pair, L> {
         }
         return Carry{a, b, (double)R};
     }
+    // outputs() times sigmoid(r): the gate's row-pair words are read into v's registers once v
+    // is spent, then traded with the partner lane.  The packed chunk has no room for float32
+    // outputs, so the gate multiplies the bf16-rounded wkv and the product is rounded again
+    // (within 1.5 bf16 units in the last place of the exact product, against 0.5 elsewhere).
+    __device__ __forceinline__ Carry outputs_gated(const Chan& ch, const Carry& c, float R, const WaveRows& w,
+                                                   bool valid) {
+        const Carry out = outputs(ch, c, R);
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) reg_fence(k[jj]);
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj)
+            v[jj] = valid ? __builtin_amdgcn_raw_buffer_load_b32(w.r, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
+                                                                 kStream)
+                          : 0u;
+        const uint32_t sel = pair_sel(w.upper);
+#pragma unroll
+        for (int jj = 0; jj < L / 2; ++jj) {
+            const uint32_t rw = pair_exchange(v[jj], w.partner, sel);
+            k[jj] = pack_bf16(bf_lo(k[jj]) * sigmoid_f(bf_lo(rw)), bf_hi(k[jj]) * sigmoid_f(bf_hi(rw)));
+        }
+        return out;
+    }
     __device__ __forceinline__ void store(const WaveRows& w, bool valid) const { store_pairs<L>(w, valid, k); }
     __device__ __forceinline__ void stash(uint32_t (*st)[64], int lane) const {
 #pragma unroll
@@ -270,7 +302,7 @@ constexpr int chunk_tokens() { return kPair<IO> ? 64 : 32; }
 // ----------------------------------------------------------------------------
 
 // grid: x covers the channels of one batch row, y is the batch row.
-template <typename IO, int L>
+template <typename IO, int L, bool GATE>
 __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
     const int C = args.C, T = args.T;
     const int bi = blockIdx.y;
@@ -289,6 +321,7 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         w.k = make_rsrc(static_cast<const char*>(args.k) + off);
         w.v = make_rsrc(static_cast<const char*>(args.v) + off);
         w.y = make_rsrc(static_cast<char*>(args.y) + off);
+        if constexpr (GATE) w.r = make_rsrc(static_cast<const char*>(args.r) + off);
         w.lane_off = (uint32_t)(c * sizeof(IO));
         w.row_bytes = (uint32_t)(C * sizeof(IO));
         Chunk<IO, L> chunk;
@@ -301,10 +334,13 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         const bool ok = nv == L && chunk_fast_ok(ch, kmax, kmin) && (st.p - (double)R <= (double)kSpan);
         if (__all(ok)) {
             chunk.weights(R);
-            st = chunk.outputs(ch, st, R);
+            if constexpr (GATE)
+                st = chunk.outputs_gated(ch, st, R, w, true);
+            else
+                st = chunk.outputs(ch, st, R);
             chunk.store(w, true);
         } else {
-            lse_walk<IO, true>(ch, st, w, nv, true, true);
+            lse_walk<IO, true, GATE>(ch, st, w, nv, true, true);
         }
     }
     if (args.sout_a) carry_to_abi(st, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
@@ -452,7 +488,7 @@ struct TileShared {
 // The tile after its k, v rows are loaded.  FAST: the wave's chunk is full and well
 // conditioned and stays in registers; otherwise the wave walks its rows in memory with
 // the exact log-sum-exp recurrence.  Both instantiations pass the same two barriers.
-template <typename IO, int L, int NW, bool FAST>
+template <typename IO, int L, int NW, bool FAST, bool GATE>
 __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Chunk<IO, L>::kStashRows>& sh,
                                           const TileRecs& recs, const WaveRows& rows, Chunk<IO, L>& chunk,
                                           const Chan& ch, float R, int lane, int wid, int ci, int bi, int c,
@@ -535,15 +571,18 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
         if (args.y == nullptr) return;  // no y: the states were all that was asked
     }
     if (FAST && __all(cin.p - (double)R <= (double)kSpan)) {
-        chunk.outputs(ch, cin, R);
+        if constexpr (GATE)
+            chunk.outputs_gated(ch, cin, R, rows, cvalid);
+        else
+            chunk.outputs(ch, cin, R);
         chunk.store(rows, cvalid);
     } else {
         Carry c2 = cin;
-        lse_walk<IO, true>(ch, c2, rows, nv, cvalid, cvalid);
+        lse_walk<IO, true, GATE>(ch, c2, rows, nv, cvalid, cvalid);
     }
 }
 
-template <typename IO, int L, int NW>
+template <typename IO, int L, int NW, bool GATE>
 __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     constexpr int TILE = L * NW;
     const int lane = threadIdx.x & 63;
@@ -573,6 +612,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
         rows.k = make_rsrc(static_cast<const char*>(args.k) + off);
         rows.v = make_rsrc(static_cast<const char*>(args.v) + off);
         rows.y = make_rsrc(static_cast<char*>(args.y) + off);
+        if constexpr (GATE) rows.r = make_rsrc(static_cast<const char*>(args.r) + off);
         rows.lane_off = (uint32_t)((c - c_grp) * sizeof(IO));
         rows.row_bytes = (uint32_t)(C * sizeof(IO));
         rows.pair_off = (uint32_t)((lane & 31) * 4) + (uint32_t)(lane >> 5) * rows.row_bytes;
@@ -600,11 +640,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     // the fast path takes full chunks only; the one ragged chunk at the end of a
     // sequence (and any ill-conditioned chunk) walks its rows exactly
     if (__all(chunk_fast_ok(ch, kmax, kmin)) && nv == L)
-        tile_body<IO, L, NW, true>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv, t_tile,
-                                   tile_len, g);
+        tile_body<IO, L, NW, true, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
+                                         t_tile, tile_len, g);
     else
-        tile_body<IO, L, NW, false>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv, t_tile,
-                                    tile_len, g);
+        tile_body<IO, L, NW, false, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
+                                          t_tile, tile_len, g);
 
     // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
     __syncthreads();
@@ -635,7 +675,10 @@ __global__ void copy_state_kernel(const float* __restrict__ ia, const float* __r
 template <typename IO>
 static hipError_t launch_seq_t(const FwdArgs& a, hipStream_t s) {
     const long blocks = (a.C + 255) / 256;
-    hipLaunchKernelGGL((fwd_seq_kernel<IO, 32>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
+    if (a.r)
+        hipLaunchKernelGGL((fwd_seq_kernel<IO, 32, true>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((fwd_seq_kernel<IO, 32, false>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -647,7 +690,10 @@ template <typename IO, int NW>
 static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
     constexpr int L = chunk_tokens<IO>();
     const long n_tiles = (long)a.n_groups * a.n_chunks;
-    hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
+    if (a.r)
+        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, true>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, false>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 

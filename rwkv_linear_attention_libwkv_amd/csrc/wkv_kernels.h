@@ -28,6 +28,7 @@ struct FwdArgs {
     const void* k;
     const void* v;
     void* y;
+    const void* r;       // optional gate [B, T, C] dtype: y becomes sigmoid(r) * wkv (null: no gate)
     const float* sin_a;  // state in, [B, C] each, or all null for the empty state
     const float* sin_b;
     const float* sin_p;
@@ -47,8 +48,8 @@ struct FwdArgs {
     int n_chunks;        // ceil(T / tile)
 };
 
-// How the chunked kernel moves k, v, y: float32 rows; bfloat16 rows at 2 bytes per lane;
-// bfloat16 row pairs at 4 bytes per lane (even C, 4-byte aligned k, v, y).  Every mode
+// How the chunked kernel moves k, v, y (and r): float32 rows; bfloat16 rows at 2 bytes per
+// lane; bfloat16 row pairs at 4 bytes per lane (even C, 4-byte aligned k, v, y, r).  Every mode
 // runs one channel per lane, 64 channels per group.
 enum IoMode { kIoF32 = 0, kIoBf16 = 1, kIoBf16Pair = 2 };
 
@@ -68,7 +69,9 @@ struct BwdArgs {
     const float* u;
     const void* k;   // [B, T, C] dtype
     const void* v;
-    const void* gy;  // dL/dy
+    const void* gy;  // dL/dy (dL/dz of the gated output z = sigmoid(r) y when r is set)
+    const void* r;   // optional gate [B, T, C] dtype (null: no gate)
+    void* gr;        // [B, T, C] dtype, dL/dr when r is set
     void* gk;        // [B, T, C] dtype
     void* gv;
     float* gw;       // [B, C] per-lane dL/dw, written by the reduction
@@ -88,6 +91,19 @@ struct BwdArgs {
 };
 // io: IoMode of k, v, gy, gk, gv (row pairs need even C and 4-byte aligned arrays).
 hipError_t launch_bwd(const BwdArgs& a, int io, hipStream_t s);
+
+// Token shift: out[m] = mu[m] x_t + (1 - mu[m]) x_{t-1} for m < M (see wkv_mix.hip).
+constexpr int kShiftMaxM = 4;
+struct ShiftArgs {
+    const void* x;       // [B, T, C] dtype
+    const void* x_prev;  // [B, C] dtype, the token before the sequence, or null (zero)
+    const float* mu;     // [M, C]
+    void* out;           // [M, B, T, C] dtype
+    int B, T, C, M;
+};
+// vec: 16-byte vectors of channels (C a multiple of 4 (f32) or 8 (bf16), 16-byte aligned x,
+// x_prev, out); otherwise one element per thread.
+hipError_t launch_token_shift(const ShiftArgs& a, int dtype, bool vec, hipStream_t s);
 
 struct StepArgs {
     const float* w;  // [G, C]

@@ -93,6 +93,7 @@ __device__ __forceinline__ void store_elt(Rsrc r, uint32_t voff, uint32_t soff, 
 // The rows of one wave: k, v, y resources based at the wave's first row and first channel.
 struct WaveRows {
     Rsrc k, v, y;
+    Rsrc r;              // gate rows when the output is sigmoid(r) * wkv (unused otherwise)
     uint32_t lane_off;   // byte offset of this lane's channel within a row
     uint32_t row_bytes;  // C * element size
     uint32_t pair_off;   // row-pair mode: byte offset of this lane's 4-byte word in a row pair
@@ -103,6 +104,9 @@ struct WaveRows {
 // ----------------------------------------------------------------------------
 // Per-token arithmetic.
 // ----------------------------------------------------------------------------
+
+// Logistic sigmoid 1 / (1 + e^{-r}) (the output gate): saturates to 0 and 1 without NaN.
+__device__ __forceinline__ float sigmoid_f(float r) { return rcp(1.f + ex2(-r * kLog2e)); }
 
 // One token of the exact log-sum-exp recurrence (any input, including huge exponent
 // ranges, negative w, Inf and NaN).  Returns y when OUT; advances c.
@@ -128,8 +132,9 @@ __device__ __forceinline__ float lse_token(const Chan& ch, Carry& c, float k, fl
 }
 
 // Exact walk over the wave's first n rows read from memory, advancing c; writes y rows
-// when OUT and `store`.  Rolled loop: this path is rare and keeps no chunk in registers.
-template <typename IO, bool OUT>
+// (sigmoid(r) * y rows when GATE) when OUT and `store`.  Rolled loop: this path is rare
+// and keeps no chunk in registers.
+template <typename IO, bool OUT, bool GATE = false>
 __device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRows& w, int n, bool load,
                                          bool store) {
 #pragma unroll 1
@@ -137,7 +142,8 @@ __device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRow
         const uint32_t so = (uint32_t)j * w.row_bytes;
         const float k = load ? load_elt<IO>(w.k, w.lane_off, so) : 0.f;
         const float v = load ? load_elt<IO>(w.v, w.lane_off, so) : 0.f;
-        const float y = lse_token<OUT>(ch, c, k, v);
+        float y = lse_token<OUT>(ch, c, k, v);
+        if constexpr (GATE) y *= sigmoid_f(load ? load_elt<IO>(w.r, w.lane_off, so) : 0.f);
         if (OUT && store) store_elt<IO>(w.y, w.lane_off, so, y);
     }
 }

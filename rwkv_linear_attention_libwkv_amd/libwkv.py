@@ -34,6 +34,9 @@ EXPORTS = (
     "wkv_saved_states_bytes",
     "wkv_forward_save",
     "wkv_backward_saved",
+    "wkv_token_shift",
+    "wkv_forward_gated",
+    "wkv_backward_gated",
     "wkv_status_string",
 )
 
@@ -80,6 +83,13 @@ def _load() -> ctypes.CDLL:
     lib.wkv_forward_save.restype = i32
     lib.wkv_backward_saved.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
     lib.wkv_backward_saved.restype = i32
+    lib.wkv_token_shift.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, vp, vp]
+    lib.wkv_token_shift.restype = i32
+    lib.wkv_forward_gated.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.wkv_forward_gated.restype = i32
+    lib.wkv_backward_gated.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
+                                       sz, vp]
+    lib.wkv_backward_gated.restype = i32
     lib.wkv_status_string.argtypes = [i32]
     lib.wkv_status_string.restype = ctypes.c_char_p
     return lib
@@ -310,6 +320,64 @@ def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=No
     return gw, gu, gk, gv
 
 
+def wkv_token_shift(x, mu, *, x_prev=None, out=None, stream=None):
+    """out[m] = mu[m] * x_t + (1 - mu[m]) * x_{t-1} for x [B, T, C], mu [M, C] float32; returns [M, B, T, C]."""
+    _need(x.dim() == 3 and x.is_cuda and x.is_contiguous(), "x must be a contiguous [B, T, C] GPU tensor")
+    B, T, C = x.shape
+    _need(mu.dim() == 2 and mu.shape[1] == C and mu.dtype == torch.float32 and mu.is_contiguous(),
+          "mu must be contiguous float32 [M, C]")
+    M = mu.shape[0]
+    if x_prev is not None:
+        _need(x_prev.shape == (B, C) and x_prev.dtype == x.dtype and x_prev.is_contiguous(), "bad x_prev")
+    out = torch.empty((M, B, T, C), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out.shape == (M, B, T, C) and out.dtype == x.dtype and out.is_contiguous(), "bad out")
+    _check(lib.wkv_token_shift(B, T, C, _dtype_code(x.dtype), _ptr(x), _ptr(x_prev), _ptr(mu), M, _ptr(out),
+                               _stream(stream)), "wkv_token_shift")
+    return out
+
+
+def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stream=None):
+    """z = sigmoid(r) * WKV(w, u, k, v).  With ``saved`` (a uint8 device tensor of
+    wkv_saved_states_bytes bytes) also keeps the states for wkv_backward_gated."""
+    _need(k.dim() == 3 and v.shape == k.shape and r.shape == k.shape, "k, v and r must be [B, T, C]")
+    _need(k.dtype == v.dtype == r.dtype, "k, v and r must share a dtype")
+    _need(k.is_contiguous() and v.is_contiguous() and r.is_contiguous() and k.is_cuda, "bad k, v or r")
+    B, T, C = k.shape
+    _need(w.numel() == C and u.numel() == C and w.dtype == torch.float32 and u.dtype == torch.float32,
+          "w and u must be float32 with C entries")
+    z = torch.empty_like(k) if z is None else z
+    _need(z.shape == k.shape and z.dtype == k.dtype and z.is_contiguous(), "bad z")
+    algo = "chunked" if saved is not None else "auto"
+    if workspace is None:
+        workspace = new_workspace(B, T, C, k.dtype, algo, 0, device=k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sb = 0 if saved is None else saved.numel() * saved.element_size()
+    _check(lib.wkv_forward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(z),
+                                 _ptr(saved), sb, _ptr(workspace), ws_bytes, _stream(stream)), "wkv_forward_gated")
+    return z
+
+
+def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=None, gw=None, gu=None,
+                       workspace=None, stream=None):
+    """Gradients of sum(gz * sigmoid(r) * WKV(w, u, k, v)): returns (gw, gu, gk, gv, gr)."""
+    _need(k.dim() == 3 and all(t.shape == k.shape for t in (v, r, gz)), "k, v, r and gz must be [B, T, C]")
+    _need(all(t.dtype == k.dtype and t.is_contiguous() and t.is_cuda for t in (v, r, gz)), "bad v, r or gz")
+    B, T, C = k.shape
+    gk = torch.empty_like(k) if gk is None else gk
+    gv = torch.empty_like(k) if gv is None else gv
+    gr = torch.empty_like(k) if gr is None else gr
+    gw = torch.empty((B, C), dtype=torch.float32, device=k.device) if gw is None else gw
+    gu = torch.empty((B, C), dtype=torch.float32, device=k.device) if gu is None else gu
+    if workspace is None:
+        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sb = 0 if saved is None else saved.numel() * saved.element_size()
+    _check(lib.wkv_backward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                  _ptr(gz), _ptr(saved), sb, _ptr(gk), _ptr(gv), _ptr(gr), _ptr(gw), _ptr(gu),
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "wkv_backward_gated")
+    return gw, gu, gk, gv, gr
+
+
 def empty_state(shape, device="cuda"):
     """(a, b, p) float32 tensors of the empty state (a = b = 0, p = P_EMPTY)."""
     a = torch.zeros(shape, dtype=torch.float32, device=device)
@@ -342,4 +410,7 @@ forward = wkv_forward
 step = wkv_step
 backward = wkv_backward
 forward_save = wkv_forward_save
+token_shift = wkv_token_shift
+forward_gated = wkv_forward_gated
+backward_gated = wkv_backward_gated
 workspace_bytes = wkv_forward_workspace_bytes

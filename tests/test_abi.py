@@ -179,6 +179,32 @@ def test_saved_state_entry_points_argument_checks():
     assert bs(2, 300, 64, F32, P, P, P, P, P, P, need, P, P, P, P, P, wsb - 1, None) == EWS
 
 
+def test_token_shift_and_gate_argument_checks():
+    ts = lib.wkv_token_shift
+    assert ts(2, 8, 16, F32, P, NULL, P, 0, P, None) == EINVAL
+    assert ts(2, 8, 16, F32, P, NULL, P, 5, P, None) == EINVAL
+    assert ts(-2, 8, 16, F32, P, NULL, P, 3, P, None) == EINVAL
+    assert ts(2, 8, 16, 4, P, NULL, P, 3, P, None) == EDTYPE
+    assert ts(2, 8, 16, F32, NULL, NULL, P, 3, P, None) == EINVAL
+    assert ts(2, 8, 16, F32, P, NULL, NULL, 3, P, None) == EINVAL
+    assert ts(2, 8, 16, F32, P, NULL, P, 3, NULL, None) == EINVAL
+    assert ts(2, 0, 16, F32, NULL, NULL, NULL, 3, NULL, None) == OK
+    fg = lib.wkv_forward_gated
+    assert fg(2, 300, 64, F32, P, P, P, P, NULL, P, NULL, 0, P, 1 << 30, None) == EINVAL
+    need = lib.wkv_saved_states_bytes(2, 300, 64)
+    assert fg(2, 300, 64, F32, P, P, P, P, P, P, P, need - 1, P, 1 << 30, None) == EINVAL
+    assert fg(2, 300, 64, 3, P, P, P, P, P, P, NULL, 0, P, 1 << 30, None) == EDTYPE
+    assert fg(0, 300, 64, F32, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, 0, None) == OK
+    bg = lib.wkv_backward_gated
+    wsb = lib.wkv_backward_workspace_bytes(2, 300, 64, F32)
+    ptrs = [P] * 4 + [NULL] + [P] + [NULL, 0] + [P] * 5
+    assert bg(2, 300, 64, F32, *ptrs, P, wsb, None) == EINVAL  # r missing
+    ptrs = [P] * 6 + [NULL, 0] + [P, P, NULL, P, P]
+    assert bg(2, 300, 64, F32, *ptrs, P, wsb, None) == EINVAL  # gr missing
+    ptrs = [P] * 6 + [NULL, 0] + [P] * 5
+    assert bg(2, 300, 64, F32, *ptrs, P, wsb - 1, None) == EWS
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import importlib
 

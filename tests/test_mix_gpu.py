@@ -1,0 +1,156 @@
+"""GPU parity of the token shift and the sigmoid(r) output gate against the float64 oracle.
+
+Gates.  Token shift: |out - ref| / (|mu| |x_t| + |1 - mu| |x_{t-1}|) at most 1e-6 for float32
+(one fma and one subtraction) and 4e-3 for bfloat16 (one rounding to bf16, 2^-8 relative at
+most).  Gated forward: |z - ref| / (sigmoid(r) s) with s the WKV scale, 2e-5 (float32) and
+1e-2 (bfloat16), the forward's gates.  Gated backward: the backward's gates, with the scale of
+dL/dr being |gz| s sigmoid(r) sigmoid(-r).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import scaled_error, token_shift, wkv_gated, wkv_gated_backward
+from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+from tests.gpu_util import TORCH_DT, host
+from tests.test_backward_gpu import TOL_BF16, TOL_F32, grad_error
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(TORCH_DT[dtype])
+
+
+def rounded(a, dtype):
+    a = np.asarray(a, dtype=np.float32)
+    return workloads.round_to_bf16(a) if dtype == "bf16" else a
+
+
+# ---- token shift ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,C,M,prev", [(2, 70, 64, 3, True), (1, 33, 40, 4, False), (3, 5, 7, 1, True),
+                                          (1, 1, 8, 2, True), (2, 100, 24, 3, False)])
+def test_token_shift(dtype, B, T, C, M, prev):
+    rng = np.random.default_rng(B * 100 + T + C + M)
+    x = rounded(rng.normal(0, 1, (B, T, C)), dtype)
+    xp = rounded(rng.normal(0, 1, (B, C)), dtype) if prev else None
+    mu = rng.uniform(-0.25, 1.25, (M, C)).astype(np.float32)
+    out = host(libwkv.wkv_token_shift(dev(x, dtype), torch.from_numpy(mu).cuda(),
+                                      x_prev=None if xp is None else dev(xp, dtype)))
+    ref = token_shift(x, mu, xp)
+    xpz = np.zeros((B, 1, C)) if xp is None else xp[:, None, :]
+    shifted = np.concatenate([xpz, x[:, :-1]], axis=1)
+    scale = np.abs(mu)[:, None, None, :] * np.abs(x)[None] + np.abs(1 - mu)[:, None, None, :] * np.abs(shifted)[None]
+    err = scaled_error(out, ref, scale)
+    print(f"  token shift {dtype} {B}x{T}x{C} M={M}: {err:.2e}", flush=True)
+    assert err <= (1e-6 if dtype == "f32" else 4e-3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_shift_vector_and_element_paths_agree(dtype):
+    """16-byte vectors (aligned, C a multiple of the vector) and one element per thread (an
+    output that is not 16-byte aligned) do the same arithmetic: bitwise equal."""
+    rng = np.random.default_rng(5)
+    B, T, C, M = 2, 67, 64, 3
+    x = dev(rng.normal(0, 1, (B, T, C)), dtype)
+    mu = torch.from_numpy(rng.uniform(0, 1, (M, C)).astype(np.float32)).cuda()
+    a = libwkv.wkv_token_shift(x, mu)
+    buf = torch.empty(M * B * T * C + 1, dtype=x.dtype, device="cuda")
+    b = libwkv.wkv_token_shift(x, mu, out=buf[1:].view(M, B, T, C))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---- gated forward ----
+
+def gate_inputs(B, T, C, seed, dtype="f32", **kw):
+    inp = workloads.backward_inputs(workloads.FWD_SMALL.with_(B=B, T=T, C=C, seed=seed, dtype=dtype, **kw))
+    rng = np.random.default_rng(seed + 99)
+    inp["r"] = rounded(rng.normal(0, 2.0, (B, T, C)), dtype)
+    return inp
+
+
+def to_dev(inp):
+    d = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).cuda() for n in ("w", "u")}
+    for n in ("k", "v", "gy", "r"):
+        d[n] = dev(inp[n], inp["dtype"])
+    return d
+
+
+@pytest.mark.parametrize("dtype,B,T,C", [("f32", 2, 300, 130), ("f32", 64, 40, 256), ("bf16", 2, 600, 192),
+                                         ("bf16", 1, 257, 67), ("f32", 1, 1, 5)])
+@pytest.mark.parametrize("save", [False, True])
+def test_gated_forward(dtype, B, T, C, save):
+    inp = gate_inputs(B, T, C, seed=T + C, dtype=dtype, k_std=1.5)
+    d = to_dev(inp)
+    saved = None
+    if save:
+        saved = torch.empty(max(4, libwkv.wkv_saved_states_bytes(B, T, C)), dtype=torch.uint8, device="cuda")
+    z = host(libwkv.wkv_forward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], saved=saved))
+    ref, scale = wkv_gated(inp["w"], inp["u"], inp["k"], inp["v"], inp["r"], return_scale=True)
+    err = scaled_error(z, ref, scale)
+    print(f"  gated forward {dtype} {B}x{T}x{C} saved={save}: {err:.2e}", flush=True)
+    assert err <= (2e-5 if dtype == "f32" else 1e-2)
+
+
+def test_gated_forward_exact_path():
+    """Ill-conditioned waves take the exact per-token path, which applies the gate too."""
+    inp = gate_inputs(2, 300, 130, seed=11)
+    inp["k"][:, ::37, ::5] = 90.0
+    inp["u"][::4] = 70.0
+    d = to_dev(inp)
+    ref, scale = wkv_gated(inp["w"], inp["u"], inp["k"], inp["v"], inp["r"], return_scale=True)
+    for algo_save in (False, True):
+        saved = torch.empty(libwkv.wkv_saved_states_bytes(2, 300, 130), dtype=torch.uint8, device="cuda") \
+            if algo_save else None
+        z = host(libwkv.wkv_forward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], saved=saved))
+        assert scaled_error(z, ref, scale) <= 2e-5
+
+
+# ---- gated backward ----
+
+@pytest.mark.parametrize("dtype,B,T,C", [("f32", 2, 300, 130), ("f32", 1, 700, 64), ("bf16", 2, 400, 128),
+                                         ("bf16", 1, 129, 67)])
+def test_gated_backward(dtype, B, T, C):
+    inp = gate_inputs(B, T, C, seed=T * 3 + C, dtype=dtype)
+    d = to_dev(inp)
+    got = [host(g) for g in libwkv.wkv_backward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], d["gy"])]
+    torch.cuda.synchronize()
+    ref, scale = wkv_gated_backward(inp["w"], inp["u"], inp["k"], inp["v"], inp["r"], inp["gy"], return_scale=True)
+    for name, g, rr, s in zip(("gw", "gu", "gk", "gv", "gr"), got, ref, scale):
+        err = grad_error(g, rr, s)
+        tol = TOL_BF16 if dtype == "bf16" and name in ("gk", "gv", "gr") else TOL_F32
+        print(f"    {dtype} {B}x{T}x{C} {name}: {err:.3e}", flush=True)
+        assert err <= tol, (name, err)
+
+
+def test_gated_backward_exact_path_and_saved_states():
+    inp = gate_inputs(2, 300, 130, seed=12)
+    inp["k"][:, 5::41, 1::7] = -90.0
+    inp["w"][::3] = -0.05
+    d = to_dev(inp)
+    ref, scale = wkv_gated_backward(inp["w"], inp["u"], inp["k"], inp["v"], inp["r"], inp["gy"], return_scale=True)
+    plain = libwkv.wkv_backward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], d["gy"])
+    saved = torch.empty(libwkv.wkv_saved_states_bytes(2, 300, 130), dtype=torch.uint8, device="cuda")
+    libwkv.wkv_forward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], saved=saved)
+    from_saved = libwkv.wkv_backward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], d["gy"], saved=saved)
+    torch.cuda.synchronize()
+    for name, a, b, rr, s in zip(("gw", "gu", "gk", "gv", "gr"), plain, from_saved, ref, scale):
+        assert torch.equal(a, b), name
+        assert grad_error(host(a), rr, s) <= TOL_F32, name
+
+
+def test_open_gate_gives_the_plain_backward():
+    """sigmoid(60) is 1 in float32: dL/dy = gz exactly, so every WKV gradient equals the
+    ungated backward's bit for bit, and dL/dr is negligible."""
+    inp = gate_inputs(2, 500, 96, seed=13)
+    d = to_dev(inp)
+    r = torch.full_like(d["k"], 60.0)
+    gw, gu, gk, gv, gr = libwkv.wkv_backward_gated(d["w"], d["u"], d["k"], d["v"], r, d["gy"])
+    ref = libwkv.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    torch.cuda.synchronize()
+    for name, a, b in zip(("gw", "gu", "gk", "gv"), (gw, gu, gk, gv), ref):
+        assert torch.equal(a, b), name
+    assert float(gr.abs().max()) < 1e-20
