@@ -9,9 +9,9 @@ with inputs resident in HBM, bracketed by torch.cuda.synchronize().  Prints one
 JSON line: elements/s (B*T*C per second), the HBM roofline of the forward kernel
 (algorithmic bytes: read k, v, write y) measured with HIP events on the launch
 stream, and the float64 CPU oracle timed on the host as a reported baseline.
-The other workloads (169M width, 64K-token bf16, the backward at the 8K-context
-and 64K-token shapes, batched decode step) are timed the same way and reported
-under "other_workloads".
+The other workloads (169M width, 64K-token bf16, the backward and the fused
+time-mixing parts at the 8K-context and 64K-token shapes, batched decode step) are
+timed the same way and reported under "other_workloads".
 """
 from __future__ import annotations
 
@@ -181,6 +181,44 @@ def backward_case(spec, steps, warmup):
     return out
 
 
+def mix_case(spec, steps, warmup):
+    """The time-mixing block's fused parts at a forward workload's shape: the token shift
+    (three mixes) and the gated forward z = sigmoid(r) * WKV, against the plain forward."""
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    elt = 4 if spec.dtype == "f32" else 2
+    rng = np.random.default_rng(spec.seed)
+    w_np, u_np = workloads.channel_params(rng, (spec.C,), spec.w_raw_lo, spec.w_raw_hi, spec.u_std)
+    w, u = torch.from_numpy(w_np).cuda(), torch.from_numpy(u_np).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(spec.seed)
+    shape = (spec.B, spec.T, spec.C)
+    k = (torch.randn(shape, generator=g, device="cuda") * spec.k_std).to(dt)
+    v = (torch.randn(shape, generator=g, device="cuda") * spec.v_std).to(dt)
+    r = torch.randn(shape, generator=g, device="cuda").to(dt)
+    z = torch.empty_like(k)
+    ws = libwkv.new_workspace(spec.B, spec.T, spec.C, dt)
+    _, per_gated = time_launches(lambda: libwkv.wkv_forward_gated(w, u, k, v, r, z=z, workspace=ws), steps, warmup)
+    mu = torch.rand((3, spec.C), generator=g, device="cuda")
+    out = torch.empty((3,) + shape, dtype=dt, device="cuda")
+    _, per_shift = time_launches(lambda: libwkv.wkv_token_shift(k, mu, out=out), steps, warmup)
+    n = spec.elements
+    res = {
+        "workload": spec.name.replace("wkv_fwd", "wkv_mix"),
+        "gated_forward_s": per_gated,
+        "gated_forward_algorithmic_GBps": 4 * elt * n / per_gated / 1e9,  # read k, v, r; write z
+        "token_shift3_s": per_shift,
+        "token_shift3_algorithmic_GBps": 4 * elt * n / per_shift / 1e9,  # read x; write three mixes
+    }
+    del k, v, r, z, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def step_case(spec, steps, warmup):
     import torch
 
@@ -319,6 +357,12 @@ def main():
             print(f"# {r['workload']}: {r['per_launch_s'] * 1e6:.1f} us/call, {r['achieved_GBps']:.0f} GB/s "
                   f"(algorithmic bytes); forward_save + backward_saved {r['train_pair_s'] * 1e6:.1f} us, "
                   f"{r['train_pair_algorithmic_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        for s in (workloads.FWD_CTX8K, workloads.FWD_LONG_BF16):
+            r = mix_case(s, max(5, args.steps // 2), 2)
+            others.append(r)
+            print(f"# {r['workload']}: gated forward {r['gated_forward_s'] * 1e6:.1f} us "
+                  f"({r['gated_forward_algorithmic_GBps']:.0f} GB/s), token shift x3 {r['token_shift3_s'] * 1e6:.1f} us "
+                  f"({r['token_shift3_algorithmic_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
         r = step_case(workloads.STEP_DECODE, args.steps, 1)
         others.append(r)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "
