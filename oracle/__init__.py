@@ -15,10 +15,13 @@ It evaluates what the pages define, slowly and plainly:
 * ``token_shift``, ``token_shift_backward`` -- the time-mixing token shift (lerp of
   x_t and x_{t-1}) and its gradients
 * ``wkv_gated``, ``wkv_gated_backward`` -- the output gate sigmoid(r) * wkv and its gradients
+* ``linear_attention_direct``, ``linear_attention_recurrent`` -- causal linear attention
+  (the linear-transformer page), masked sums and cumulative-state forms
 * ``scaled_error``    -- the scale-normalised error used as the parity gate
 
 Citations name the page ("Reinventing RNNs for the Transformer Era: RWKV",
-a paper review on velog) and its section/equation.
+a paper review on velog, or the linear-transformer review "Transformers are
+RNNs: ...") and its section/equation.
 """
 from .wkv_oracle import (  # noqa: F401
     EMPTY_P,
@@ -32,4 +35,5 @@ from .wkv_oracle import (  # noqa: F401
 )
 from .wkv_mp import wkv_mp  # noqa: F401
 from .wkv_grad import wkv_backward_direct  # noqa: F401
+from .linear_attention import elu_feature, linear_attention_direct, linear_attention_recurrent  # noqa: F401
 from .wkv_mix import sigmoid, token_shift, token_shift_backward, wkv_gated, wkv_gated_backward  # noqa: F401

@@ -93,6 +93,37 @@ STEP_DECODE = StepSpec("wkv_step_bf16_N256_G32_C4096_x16", 256, 32, 4096, steps=
 FORWARD_SPECS = {s.name: s for s in (FWD_SMALL, FWD_169M, FWD_CTX8K, FWD_LONG_BF16)}
 
 
+@dataclass(frozen=True)
+class LinearAttnSpec:
+    """Causal linear attention: q, k [BH, N, D], v and the output [BH, N, M] (BH = batch x heads)."""
+
+    name: str
+    BH: int
+    N: int
+    D: int
+    M: int
+    dtype: str = "f32"
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.BH * self.N
+
+    def with_(self, **kw) -> "LinearAttnSpec":
+        return dataclasses.replace(self, **kw)
+
+
+# Shapes of the linear-transformer page's experiments: 8 heads of 32 dimensions (embedding
+# 256); MNIST generation (784 pixels, batch 10), CIFAR-10 generation (3072 values, batch 4),
+# and the long-sequence scaling runs (up to 2^14 positions at which the baselines still ran).
+LA_SMALL = LinearAttnSpec("la_f32_BH2_N300_D32_M32", 2, 300, 32, 32)
+LA_MNIST = LinearAttnSpec("la_f32_BH80_N784_D32_M32", 80, 784, 32, 32)
+LA_CIFAR = LinearAttnSpec("la_f32_BH32_N3072_D32_M32", 32, 3072, 32, 32)
+LA_LONG = LinearAttnSpec("la_f32_BH64_N16384_D32_M32", 64, 16384, 32, 32)
+LA_LONG_BF16 = LinearAttnSpec("la_bf16_BH64_N16384_D32_M32", 64, 16384, 32, 32, "bf16")
+LA_SPECS = {s.name: s for s in (LA_SMALL, LA_MNIST, LA_CIFAR, LA_LONG, LA_LONG_BF16)}
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -141,6 +172,17 @@ def backward_inputs(spec: ForwardSpec) -> dict:
     gy = rng.standard_normal(size=(spec.B, spec.T, spec.C), dtype=np.float32)
     inp["gy"] = round_to_bf16(gy) if spec.dtype == "bf16" else gy
     return inp
+
+
+def linear_attention_inputs(spec: LinearAttnSpec) -> dict:
+    """q, k, v ~ N(0, 1) as float32 (bf16-representable for bf16 workloads), drawn in that order
+    from default_rng(seed)."""
+    rng = np.random.default_rng(spec.seed)
+    out = {"dtype": spec.dtype}
+    for name, last in (("q", spec.D), ("k", spec.D), ("v", spec.M)):
+        x = rng.standard_normal(size=(spec.BH, spec.N, last), dtype=np.float32)
+        out[name] = round_to_bf16(x) if spec.dtype == "bf16" else x
+    return out
 
 
 def step_params(spec: StepSpec) -> tuple:
