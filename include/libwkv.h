@@ -271,6 +271,30 @@ wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Causal linear attention, the second workload (page "Transformers are RNNs:
+ * 선형 어텐션으로 만드는 빠른 자기회귀 트랜스포머", sections "인과 마스킹과 누적합" and
+ * "특징 맵 선택과 계산 비용"): for every sequence b < BH (batch x heads) and
+ * position i,
+ *   out_i = sum_{j<=i} phi(q_i).phi(k_j) v_j / sum_{j<=i} phi(q_i).phi(k_j),
+ * with phi(x) = elu(x) + 1 applied elementwise when feature_map is non-zero,
+ * and q, k used as given (they must then be positive) when it is zero.
+ *   q, k : [BH, N, D], v, out : [BH, N, M], dtype dt, dense row-major.
+ * D = M = 32 and D = M = 64 are supported (WKV_EINVAL otherwise).  float32
+ * inputs use float32 matrix cores; bfloat16 inputs use bf16 matrix cores with
+ * float32 accumulation (phi, the masked similarities and the carried state
+ * are rounded to bf16 as operands).  ws: device workspace of
+ * wkv_linear_attention_workspace_bytes(...) bytes (no initialisation needed;
+ * the call overwrites it).  Keys below about -87 underflow phi in float32.
+ */
+size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M,
+                                            wkv_dtype dt);
+
+wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt,
+                                const void* q, const void* k, const void* v, void* out,
+                                int feature_map, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
  * One RNN-mode decoding step for N sequences x G layer slots x C channels
  * (section "RNN-유사추론" equation, and steps 4 and 7 of its decoding list:
  * update the WKV state, then store it for the next token).

@@ -4,6 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <climits>
 
 #include "libwkv.h"
@@ -418,6 +419,41 @@ wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const 
     a.C = (int)C;
     a.M = (int)M;
     return wkv::launch_token_shift(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
+size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
+    if (BH < 0 || N < 0 || !dtype_ok(dt)) return (size_t)-1;
+    if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return (size_t)-1;
+    if (BH == 0 || N == 0) return 0;
+    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    return (size_t)BH * (size_t)n_chunks * (size_t)(D * M + D) * 4 + kAlign;
+}
+
+wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt, const void* q,
+                                const void* k, const void* v, void* out, int feature_map, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    if (BH < 0 || N < 0 || BH > INT_MAX || N > INT_MAX) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return WKV_EINVAL;
+    if (BH == 0 || N == 0) return WKV_OK;
+    if (!q || !k || !v || !out) return WKV_EINVAL;
+    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    if (BH * n_chunks > INT_MAX || BH * N * std::max(D, M) > ((int64_t)1 << 40)) return WKV_EINVAL;
+    const size_t need = wkv_linear_attention_workspace_bytes(BH, N, D, M, dt);
+    if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
+    wkv::LaArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.agg = reinterpret_cast<float*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    a.BH = (int)BH;
+    a.N = (int)N;
+    a.D = (int)D;
+    a.M = (int)M;
+    a.n_chunks = (int)n_chunks;
+    a.feature = feature_map ? 1 : 0;
+    return wkv::launch_linear_attention(a, dt == WKV_F32 ? 0 : 1, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

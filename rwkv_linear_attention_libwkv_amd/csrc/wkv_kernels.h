@@ -105,6 +105,21 @@ struct ShiftArgs {
 // x_prev, out); otherwise one element per thread.
 hipError_t launch_token_shift(const ShiftArgs& a, int dtype, bool vec, hipStream_t s);
 
+// Causal linear attention (see la_forward.hip): q, k [BH, N, D], v, out [BH, N, M] of one dtype.
+struct LaArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* agg;    // [BH][n_chunks][D * M + D] chunk aggregates, then their exclusive prefix
+    int BH, N, D, M;
+    int n_chunks;  // ceil(N / la_chunk_len(D, M))
+    int feature;   // apply phi = elu + 1 to q and k
+};
+// Positions per chunk for these head sizes (only D = M = 32 and D = M = 64 are built).
+int la_chunk_len(int D, int M);
+hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s);
+
 struct StepArgs {
     const float* w;  // [G, C]
     const float* u;

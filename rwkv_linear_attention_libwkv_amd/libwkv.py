@@ -37,6 +37,8 @@ EXPORTS = (
     "wkv_token_shift",
     "wkv_forward_gated",
     "wkv_backward_gated",
+    "wkv_linear_attention_workspace_bytes",
+    "wkv_linear_attention",
     "wkv_status_string",
 )
 
@@ -90,6 +92,10 @@ def _load() -> ctypes.CDLL:
     lib.wkv_backward_gated.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
     lib.wkv_backward_gated.restype = i32
+    lib.wkv_linear_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.wkv_linear_attention_workspace_bytes.restype = sz
+    lib.wkv_linear_attention.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.wkv_linear_attention.restype = i32
     lib.wkv_status_string.argtypes = [i32]
     lib.wkv_status_string.restype = ctypes.c_char_p
     return lib
@@ -376,6 +382,28 @@ def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=No
                                   _ptr(gz), _ptr(saved), sb, _ptr(gk), _ptr(gv), _ptr(gr), _ptr(gw), _ptr(gu),
                                   _ptr(workspace), ws_bytes, _stream(stream)), "wkv_backward_gated")
     return gw, gu, gk, gv, gr
+
+
+def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, stream=None):
+    """Causal linear attention for q, k [BH, N, D] and v [BH, N, M] (float32 or bfloat16)."""
+    _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
+          "q, k must be [BH, N, D] and v [BH, N, M]")
+    _need(q.dtype == k.dtype == v.dtype and all(t.is_cuda and t.is_contiguous() for t in (q, k, v)),
+          "q, k, v must be contiguous GPU tensors of one dtype")
+    BH, N, D = q.shape
+    M = v.shape[2]
+    out = torch.empty_like(v) if out is None else out
+    _need(out.shape == v.shape and out.dtype == v.dtype and out.is_contiguous(), "bad out")
+    need = lib.wkv_linear_attention_workspace_bytes(BH, N, D, M, _dtype_code(q.dtype))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wkv_linear_attention(BH, N, D, M, _dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                    1 if feature_map else 0, _ptr(workspace), ws_bytes, _stream(stream)),
+           "wkv_linear_attention")
+    return out
 
 
 def empty_state(shape, device="cuda"):

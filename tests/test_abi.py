@@ -205,6 +205,23 @@ def test_token_shift_and_gate_argument_checks():
     assert bg(2, 300, 64, F32, *ptrs, P, wsb - 1, None) == EWS
 
 
+def test_linear_attention_argument_checks():
+    la = lib.wkv_linear_attention
+    q = lib.wkv_linear_attention_workspace_bytes
+    bad = ctypes.c_size_t(-1).value
+    assert q(4, 100, 32, 32, F32) > 0 and q(4, 100, 48, 48, F32) == bad and q(4, 100, 32, 64, F32) == bad
+    assert q(-1, 100, 32, 32, F32) == bad and q(4, 100, 32, 32, 7) == bad and q(0, 100, 32, 32, F32) == 0
+    need = q(4, 100, 32, 32, BF16)
+    assert la(4, 100, 48, 48, F32, P, P, P, P, 1, P, need, None) == EINVAL
+    assert la(4, 100, 32, 32, 9, P, P, P, P, 1, P, need, None) == EDTYPE
+    assert la(-4, 100, 32, 32, F32, P, P, P, P, 1, P, need, None) == EINVAL
+    assert la(4, 100, 32, 32, F32, NULL, P, P, P, 1, P, need, None) == EINVAL
+    assert la(4, 100, 32, 32, F32, P, P, P, NULL, 1, P, need, None) == EINVAL
+    assert la(4, 100, 32, 32, F32, P, P, P, P, 1, NULL, 0, None) == EWS
+    assert la(4, 100, 32, 32, F32, P, P, P, P, 1, P, need - 1, None) == EWS
+    assert la(0, 100, 32, 32, F32, NULL, NULL, NULL, NULL, 1, NULL, 0, None) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import importlib
 
