@@ -10,8 +10,9 @@ JSON line: elements/s (B*T*C per second), the HBM roofline of the forward kernel
 (algorithmic bytes: read k, v, write y) measured with HIP events on the launch
 stream, and the float64 CPU oracle timed on the host as a reported baseline.
 The other workloads (169M width, 64K-token bf16, the backward and the fused
-time-mixing parts at the 8K-context and 64K-token shapes, batched decode step) are
-timed the same way and reported under "other_workloads".
+time-mixing parts at the 8K-context and 64K-token shapes, causal linear attention at
+the linear-transformer page's shapes, batched decode step) are timed the same way and
+reported under "other_workloads".
 """
 from __future__ import annotations
 
@@ -219,6 +220,40 @@ def mix_case(spec, steps, warmup):
     return res
 
 
+def la_case(spec, steps, warmup):
+    """wkv_linear_attention on one of the linear-transformer page's shapes."""
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv
+
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(spec.seed)
+    q = torch.randn((spec.BH, spec.N, spec.D), generator=g, device="cuda").to(dt)
+    k = torch.randn((spec.BH, spec.N, spec.D), generator=g, device="cuda").to(dt)
+    v = torch.randn((spec.BH, spec.N, spec.M), generator=g, device="cuda").to(dt)
+    out = torch.empty_like(v)
+    need = libwkv.lib.wkv_linear_attention_workspace_bytes(spec.BH, spec.N, spec.D, spec.M, 0 if spec.dtype == "f32" else 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _, per = time_launches(lambda: libwkv.linear_attention(q, k, v, out=out, workspace=ws), steps, warmup)
+    elt = 4 if spec.dtype == "f32" else 2
+    nbytes = spec.tokens * (2 * spec.D + 2 * spec.M) * elt  # read q, k, v; write out
+    # similarities (causal half of each 32 x 32 block), their product with v, the carried state
+    # product, and the sub-chunk aggregate (counted twice: aggregate pass and output pass)
+    flops = 2 * spec.tokens * (16 * spec.D + 16 * spec.M + 3 * spec.D * spec.M)
+    res = {
+        "workload": spec.name,
+        "per_call_s": per,
+        "tokens_per_s": spec.tokens / per,
+        "algorithmic_bytes_per_call": nbytes,
+        "achieved_GBps": nbytes / per / 1e9,
+        "useful_TFLOPs": flops / per / 1e12,
+    }
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def step_case(spec, steps, warmup):
     import torch
 
@@ -296,6 +331,9 @@ def profile_run(name, launches):
         spec = workloads.FORWARD_SPECS[name]
         r = forward_case(spec, launches, 1, gen="torch")
         print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch", flush=True)
+    elif name in workloads.LA_SPECS:
+        r = la_case(workloads.LA_SPECS[name], launches, 1)
+        print(f"# {name}: {r['per_call_s'] * 1e6:.1f} us/call", flush=True)
     elif name.replace("wkv_bwd", "wkv_fwd") in workloads.FORWARD_SPECS:
         spec = workloads.FORWARD_SPECS[name.replace("wkv_bwd", "wkv_fwd")]
         r = backward_case(spec, launches, 1)
@@ -363,6 +401,13 @@ def main():
             print(f"# {r['workload']}: gated forward {r['gated_forward_s'] * 1e6:.1f} us "
                   f"({r['gated_forward_algorithmic_GBps']:.0f} GB/s), token shift x3 {r['token_shift3_s'] * 1e6:.1f} us "
                   f"({r['token_shift3_algorithmic_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
+        for s in workloads.LA_SPECS.values():
+            if s.tokens < 100000:
+                continue
+            r = la_case(s, max(5, args.steps // 2), 2)
+            others.append(r)
+            print(f"# {r['workload']}: {r['per_call_s'] * 1e6:.1f} us, {r['achieved_GBps']:.0f} GB/s, "
+                  f"{r['useful_TFLOPs']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         r = step_case(workloads.STEP_DECODE, args.steps, 1)
         others.append(r)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "

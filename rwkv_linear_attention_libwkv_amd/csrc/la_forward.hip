@@ -16,7 +16,8 @@
 // Three launches: la_chunk_kernel<0> writes each chunk's aggregate (phi(K)^T V, sum phi(K));
 // la_scan_kernel turns them, per sequence and entry, into the exclusive prefix (the state
 // entering each chunk, summed in chunk order); la_chunk_kernel<1> recomputes the sub-chunk
-// aggregates, adds them in wave order to the chunk's entering state, and writes the outputs.
+// aggregates, adds them in wave order to the chunk's entering state (each workgroup thread
+// taking a slice of the entries), and writes the outputs.
 // Every sum has a fixed order, so results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,30 +43,92 @@ __device__ __forceinline__ float ld(const IO* p) {
         return bf_lo((uint32_t)*reinterpret_cast<const uint16_t*>(p));
 }
 
-// acc += A (16 x K) B (K x 16) for this lane's tile slot: fa(i, k) and fb(k, n) give the
-// operands; lane (g = lane / 16, r = lane % 16) supplies row i = r of A and column n = r of B.
-// float32: 16x16x4 steps; group g takes the k block [g K/4, (g+1) K/4) one k per step.
-// bfloat16: 16x16x32 steps; group g takes k = 32 s + 8 g + j, j < 8.
-template <typename IO, int K, typename FA, typename FB>
-__device__ __forceinline__ f32x4v tile_mma(f32x4v acc, int lane, FA fa, FB fb) {
-    const int g = lane >> 4, r = lane & 15;
+// Eight consecutive elements (32 or 16 bytes, aligned) as floats; zeros when !ok.
+typedef float f32x4a __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
+template <typename IO>
+__device__ __forceinline__ void load8(const IO* p, bool ok, float (&x)[8]) {
     if constexpr (sizeof(IO) == 4) {
-        static_assert(K % 4 == 0, "K");
+        f32x4a a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            a = *reinterpret_cast<const f32x4a*>(p);
+            b = *reinterpret_cast<const f32x4a*>(p + 4);
+        }
 #pragma unroll
-        for (int s = 0; s < K / 4; ++s) {
-            const int k = g * (K / 4) + s;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, k), fb(k, r), acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+            x[j] = a[j];
+            x[4 + j] = b[j];
         }
     } else {
-        static_assert(K % 32 == 0, "K");
+        u32x4a a = {0u, 0u, 0u, 0u};
+        if (ok) a = *reinterpret_cast<const u32x4a*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf_lo(a[j]);
+            x[2 * j + 1] = bf_hi(a[j]);
+        }
+    }
+}
+
+// Rows [0, nv) of a 32 x W block (W elements per row, from src) into st[32][W + 1] as float,
+// phi applied when `feat`; rows beyond nv are zero.  Each lane moves runs of four elements
+// (16-byte float32 or 8-byte bf16 loads), so a wave reads whole rows.
+template <typename IO, int W>
+__device__ __forceinline__ void stage_rows(const IO* src, int nv, float* st, bool feat, int lane) {
+    constexpr int VPR = W / 4;  // runs per row
+#pragma unroll
+    for (int i = lane; i < kLaSub * VPR; i += 64) {
+        const int t = i / VPR, c = 4 * (i % VPR);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < nv) {
+            if constexpr (sizeof(IO) == 4) {
+                const f32x4a a = *reinterpret_cast<const f32x4a*>(src + t * W + c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = feat ? elu1(a[j]) : a[j];
+            } else {
+                typedef uint32_t u32x2a __attribute__((ext_vector_type(2)));
+                const u32x2a a = *reinterpret_cast<const u32x2a*>(src + t * W + c);
+                x[0] = bf_lo(a[0]);
+                x[1] = bf_hi(a[0]);
+                x[2] = bf_lo(a[1]);
+                x[3] = bf_hi(a[1]);
+                if (feat)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = elu1(x[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[t * (W + 1) + c + j] = x[j];
+    }
+}
+
+// Operands of a 16 x 16 x K tile product held in registers: each lane keeps K/4 elements of
+// its A row (i = lane % 16) and of its B column (n = lane % 16).  Element e of lane group
+// g = lane / 16 stands for k = kidx(g, e): float32 (16x16x4 steps, one k per step) uses the
+// block [g K/4, (g+1) K/4); bfloat16 (16x16x32 steps, eight k per step) uses
+// k = 32 (e / 8) + 8 g + e % 8.  Both A and B use the same map, so the products pair up;
+// the map makes a lane's q and k elements contiguous in memory.
+template <typename IO, int K>
+__device__ __forceinline__ int kidx(int g, int e) {
+    if constexpr (sizeof(IO) == 4)
+        return g * (K / 4) + e;
+    else
+        return 32 * (e / 8) + 8 * g + (e % 8);
+}
+
+template <typename IO, int K>
+__device__ __forceinline__ f32x4v mma(f32x4v acc, const float (&x)[K / 4], const float (&y)[K / 4]) {
+    if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+        for (int e = 0; e < K / 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
+    } else {
 #pragma unroll
         for (int s = 0; s < K / 32; ++s) {
             bf16x8v a, b;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int k = 32 * s + 8 * g + j;
-                a[j] = (__bf16)fa(r, k);
-                b[j] = (__bf16)fb(k, r);
+                a[j] = (__bf16)x[8 * s + j];
+                b[j] = (__bf16)y[8 * s + j];
             }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
         }
@@ -73,22 +136,37 @@ __device__ __forceinline__ f32x4v tile_mma(f32x4v acc, int lane, FA fa, FB fb) {
     return acc;
 }
 
-template <int D, int M, int NW>
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// One region per wave holds in turn the sub-chunk's phi(K) and V rows (staged with 16-byte
+// loads, read back in the operand layouts), its aggregate phi(K)^T V (D x M) and, once every
+// wave has read the aggregates it needs, the masked similarities (32 x 32).
+template <int D, int M, int NW, int PHASE>
 struct LaShared {
-    float S[NW][D][M + 1];  // sub-chunk aggregates, then each wave's entering state
-    float z[NW][D];
-    float A[NW][kLaSub][kLaSub + 1];  // masked similarities of each sub-chunk
-    float den[NW][kLaSub];
+    static constexpr int kRegion =
+        cmax(kLaSub * (D + 1) + kLaSub * (M + 1), cmax(D * (M + 1), kLaSub * (kLaSub + 1)));
+    float R[NW][kRegion];
+    float z[NW][D];                       // sub-chunk sums of phi(K)
+    float den[PHASE ? NW : 1][kLaSub];    // phi(q_t) . z entering the sub-chunk
+    __device__ __forceinline__ float& S(int w, int d, int m) { return R[w][d * (M + 1) + m]; }
+    __device__ __forceinline__ float& A(int w, int t, int c) { return R[w][t * (kLaSub + 1) + c]; }
 };
+
+// sum of x over the lanes reached by xor with lo, 2 lo, ..., hi (a butterfly)
+__device__ __forceinline__ float sum_lanes(float x, int lo, int hi) {
+    for (int m = lo; m <= hi; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
 
 // PHASE 0: chunk aggregates into a.agg.  PHASE 1: outputs from the chunk's entering state.
 template <typename IO, int D, int M, int NW, int PHASE>
 __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     constexpr int CH = kLaSub * NW;
+    constexpr int ET = kLaSub / 4, ED = D / 4;  // operand elements per lane: token / feature contractions
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, r = lane & 15;
-    __shared__ LaShared<D, M, NW> sh;
+    __shared__ LaShared<D, M, NW, PHASE> sh;
 
     const int bh = blockIdx.x / a.n_chunks;
     const int ci = blockIdx.x % a.n_chunks;
@@ -99,116 +177,149 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     const IO* k = static_cast<const IO*>(a.k) + row0 * D;
     const IO* v = static_cast<const IO*>(a.v) + row0 * M;
     const bool feat = a.feature != 0;
+    auto phi = [&](float x) { return feat ? elu1(x) : x; };
 
-    // rows at or beyond nv contribute nothing (phi(k) = 0 and v = 0 there)
-    auto phik = [&](int t, int d) -> float {
-        if (t >= nv) return 0.f;
-        const float x = ld<IO>(k + t * D + d);
-        return feat ? elu1(x) : x;
-    };
-    auto phiq = [&](int t, int d) -> float {
-        if (t >= nv) return 0.f;
-        const float x = ld<IO>(q + t * D + d);
-        return feat ? elu1(x) : x;
-    };
-    auto val = [&](int t, int m) -> float { return t < nv ? ld<IO>(v + t * M + m) : 0.f; };
+    // ---- stage this sub-chunk's phi(K) and V rows in the wave's region (zero beyond nv) ----
+    float* sk = sh.R[wid];                      // [32][D + 1]
+    float* sv = sh.R[wid] + kLaSub * (D + 1);   // [32][M + 1]
+    stage_rows<IO, D>(k, nv, sk, feat, lane);
+    stage_rows<IO, M>(v, nv, sv, false, lane);
 
-    // ---- this sub-chunk's aggregate phi(K)^T V (D x M) and sum phi(K) ----
+    // ---- operands: phi(K) as A (rows d, k = t) and V as B (k = t, columns m) ----
+    float ka[D / 16][ET], vb[M / 16][ET];
 #pragma unroll
-    for (int dI = 0; dI < D / 16; ++dI)
+    for (int e = 0; e < ET; ++e) {
+        const int t = kidx<IO, kLaSub>(g, e);
+#pragma unroll
+        for (int dI = 0; dI < D / 16; ++dI) ka[dI][e] = sk[t * (D + 1) + 16 * dI + r];
+#pragma unroll
+        for (int mJ = 0; mJ < M / 16; ++mJ) vb[mJ][e] = sv[t * (M + 1) + 16 * mJ + r];
+    }
+    // phi(Q) as A (rows t, k = d; from memory: a lane's elements of a row are runs of 8
+    // consecutive features, read with 16-byte loads) and phi(K) as B (k = d, columns t)
+    float qa[2][ED], kb[2][ED];
+    if constexpr (PHASE == 1) {
+#pragma unroll
+        for (int tI = 0; tI < 2; ++tI) {
+            const int t = 16 * tI + r;
+#pragma unroll
+            for (int e8 = 0; e8 < ED; e8 += 8) {
+                const int d = kidx<IO, D>(g, e8);  // first of 8 consecutive features
+                float xq[8];
+                load8<IO>(q + t * D + d, t < nv, xq);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    qa[tI][e8 + j] = t < nv ? phi(xq[j]) : 0.f;
+                    kb[tI][e8 + j] = sk[t * (D + 1) + d + j];
+                }
+            }
+        }
+    }
+
+    // ---- sub-chunk aggregate phi(K)^T V and sum phi(K) ----
+#pragma unroll
+    for (int dI = 0; dI < D / 16; ++dI) {
 #pragma unroll
         for (int mJ = 0; mJ < M / 16; ++mJ) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<IO, kLaSub>(acc, lane, [&](int i, int t) { return phik(t, 16 * dI + i); },
-                                       [&](int t, int n) { return val(t, 16 * mJ + n); });
+            acc = mma<IO, kLaSub>(acc, ka[dI], vb[mJ]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sh.S[wid][16 * dI + 4 * g + j][16 * mJ + r] = acc[j];
+            for (int j = 0; j < 4; ++j) sh.S(wid, 16 * dI + 4 * g + j, 16 * mJ + r) = acc[j];
         }
-    for (int d = lane; d < D; d += 64) {
-        float s = 0.f;
-        for (int t = 0; t < nv; ++t) s += phik(t, d);
-        sh.z[wid][d] = s;
+        float zs = 0.f;
+#pragma unroll
+        for (int e = 0; e < ET; ++e) zs += ka[dI][e];
+        zs = sum_lanes(zs, 16, 32);
+        if (g == 0) sh.z[wid][16 * dI + r] = zs;
     }
-    __syncthreads();
 
     const size_t rec = (size_t)D * M + D;  // floats per chunk record
     float* agg = a.agg + ((size_t)bh * a.n_chunks + ci) * rec;
     if constexpr (PHASE == 0) {
+        __syncthreads();
         // chunk aggregate: the sub-chunk aggregates added in wave order
         for (int e = threadIdx.x; e < (int)rec; e += 64 * NW) {
             float s = 0.f;
-            for (int w = 0; w < NW; ++w) s += e < D * M ? sh.S[w][e / M][e % M] : sh.z[w][e - D * M];
+            for (int w = 0; w < NW; ++w) s += e < D * M ? sh.S(w, e / M, e % M) : sh.z[w][e - D * M];
             agg[e] = s;
         }
-        return;
     } else {
-        // ---- each wave's entering state: the chunk's (exclusive prefix) plus the waves before ----
-        constexpr int PER = (D * M + 63) / 64;
-        float st[PER];
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = lane + 64 * p;
-            float s = 0.f;
-            if (e < D * M) {
-                s = agg[e];
-                for (int w = 0; w < wid; ++w) s += sh.S[w][e / M][e % M];
-            }
-            st[p] = s;
-        }
-        float zs = 0.f;
-        if (lane < D) {
-            zs = agg[D * M + lane];
-            for (int w = 0; w < wid; ++w) zs += sh.z[w][lane];
-        }
-        __syncthreads();  // every wave has read the aggregates
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = lane + 64 * p;
-            if (e < D * M) sh.S[wid][e / M][e % M] = st[p];
-        }
-        if (lane < D) sh.z[wid][lane] = zs;
+        __syncthreads();  // every wave's aggregate is in LDS
 
-        // ---- masked similarities phi(Q) phi(K)^T (32 x 32) ----
+        // ---- the state entering each wave: the chunk's plus the waves before, in wave order;
+        // the entries are split across all the workgroup's threads and replaced in place ----
+        for (int e = threadIdx.x; e < (int)rec; e += 64 * NW) {
+            float run = agg[e];
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI)
+            for (int w = 0; w < NW; ++w) {
+                float& x = e < D * M ? sh.S(w, e / M, e % M) : sh.z[w][e - D * M];
+                const float dx = x;
+                x = run;
+                run += dx;
+            }
+        }
+        __syncthreads();
+        float sb[M / 16][ED], zb[ED];  // as B operand (k = d, columns m)
+#pragma unroll
+        for (int e = 0; e < ED; ++e) {
+            const int d = kidx<IO, D>(g, e);
+#pragma unroll
+            for (int mJ = 0; mJ < M / 16; ++mJ) sb[mJ][e] = sh.S(wid, d, 16 * mJ + r);
+            zb[e] = sh.z[wid][d];
+        }
+        // phi(q_t) . z for the rows t = 16 tI + r
+#pragma unroll
+        for (int tI = 0; tI < 2; ++tI) {
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < ED; ++e) p = fmaf(qa[tI][e], zb[e], p);
+            p = sum_lanes(p, 16, 32);
+            if (g == 0) sh.den[wid][16 * tI + r] = p;
+        }
+        __syncthreads();  // every wave has read the aggregates: the regions take the similarities
+
+        // ---- masked similarities phi(Q) phi(K)^T (32 x 32) and their row sums ----
+        float rs[2][4];
+#pragma unroll
+        for (int tI = 0; tI < 2; ++tI) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rs[tI][j] = 0.f;
 #pragma unroll
             for (int tJ = 0; tJ < 2; ++tJ) {
                 f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-                if (tJ <= tI)
-                    acc = tile_mma<IO, D>(acc, lane, [&](int i, int d) { return phiq(16 * tI + i, d); },
-                                          [&](int d, int n) { return phik(16 * tJ + n, d); });
+                if (tJ <= tI) acc = mma<IO, D>(acc, qa[tI], kb[tJ]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * tI + 4 * g + j, col = 16 * tJ + r;
-                    sh.A[wid][row][col] = col <= row ? acc[j] : 0.f;
+                    const float x = col <= row ? acc[j] : 0.f;
+                    sh.A(wid, row, col) = x;
+                    rs[tI][j] += x;
                 }
             }
-        __syncthreads();
-        // denominators, one position per lane
-        if (lane < kLaSub) {
-            float s = 0.f;
-            for (int c = 0; c <= lane; ++c) s += sh.A[wid][lane][c];
-            for (int d = 0; d < D; ++d) s = fmaf(phiq(lane, d), sh.z[wid][d], s);
-            sh.den[wid][lane] = s;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rs[tI][j] = sum_lanes(rs[tI][j], 1, 8);
         }
         __syncthreads();
 
         // ---- outputs: (tril(A) V + phi(Q) S_w) / den ----
         IO* out = static_cast<IO*>(a.out) + row0 * M;
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI)
+        for (int tI = 0; tI < 2; ++tI) {
+            float aa[ET], inv[4];
+#pragma unroll
+            for (int e = 0; e < ET; ++e) aa[e] = sh.A(wid, 16 * tI + r, kidx<IO, kLaSub>(g, e));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) inv[j] = 1.f / (rs[tI][j] + sh.den[wid][16 * tI + 4 * g + j]);
 #pragma unroll
             for (int mJ = 0; mJ < M / 16; ++mJ) {
                 f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-                acc = tile_mma<IO, kLaSub>(acc, lane, [&](int i, int t) { return sh.A[wid][16 * tI + i][t]; },
-                                           [&](int t, int n) { return val(t, 16 * mJ + n); });
-                acc = tile_mma<IO, D>(acc, lane, [&](int i, int d) { return phiq(16 * tI + i, d); },
-                                      [&](int d, int n) { return sh.S[wid][d][16 * mJ + n]; });
+                acc = mma<IO, kLaSub>(acc, aa, vb[mJ]);
+                acc = mma<IO, D>(acc, qa[tI], sb[mJ]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * tI + 4 * g + j, col = 16 * mJ + r;
                     if (row < nv) {
-                        const float y = acc[j] / sh.den[wid][row];
+                        const float y = acc[j] * inv[j];
                         if constexpr (sizeof(IO) == 4)
                             reinterpret_cast<float*>(out)[row * M + col] = y;
                         else
@@ -216,6 +327,7 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
                     }
                 }
             }
+        }
     }
 }
 
