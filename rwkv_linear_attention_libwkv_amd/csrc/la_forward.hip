@@ -339,10 +339,16 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int rec) {
     const long bh = i / rec, e = i % rec;
     float* p = a.agg + (size_t)bh * a.n_chunks * rec + e;
     float run = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) {
-        const float x = p[(size_t)c * rec];
-        p[(size_t)c * rec] = run;
-        run += x;
+    // eight chunks' loads in flight at a time; the sums stay in chunk order
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = c0 + j < a.n_chunks ? p[(size_t)(c0 + j) * rec] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (c0 + j < a.n_chunks) p[(size_t)(c0 + j) * rec] = run;
+            run += x[j];
+        }
     }
 }
 
