@@ -33,6 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("wkv_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h",
                   "libwkv_api.cpp")
 BACKWARD_SOURCES = KERNEL_SOURCES + ("wkv_backward.hip",)
+LA_SOURCES = ("la_forward.hip", "wkv_rows.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -248,6 +249,7 @@ def la_case(spec, steps, warmup):
         "algorithmic_bytes_per_call": nbytes,
         "achieved_GBps": nbytes / per / 1e9,
         "useful_TFLOPs": flops / per / 1e12,
+        "traffic_bytes_per_call": measured_traffic(spec.name, LA_SOURCES),
     }
     del q, k, v, out, ws
     torch.cuda.empty_cache()
