@@ -77,6 +77,45 @@ def time_launches(fn, steps, warmup):
     return wall, ev / steps
 
 
+def per_launch_stats(fn, n=20, flush=None):
+    """Median and min of n single launches, each timed with its own HIP events on the launch
+    stream.  flush: a callable run (and synchronized) before every launch, e.g. a write of a
+    buffer larger than the 256 MB last-level cache so that the launch starts cold."""
+    import numpy as np
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    return {"median_s": float(np.median(ts)), "min_s": float(np.min(ts)), "n": n}
+
+
+CACHE_FLUSH_BYTES = 512 << 20  # twice the MI355X last-level (MALL) cache
+
+
+def cache_flusher():
+    import torch
+
+    buf = torch.empty(CACHE_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    state = {"i": 0}
+
+    def flush():
+        state["i"] += 1
+        buf.fill_(float(state["i"]))
+
+    return flush, buf
+
+
 def forward_case(spec, steps, warmup, gen="numpy"):
     import numpy as np
     import torch
@@ -107,20 +146,30 @@ def forward_case(spec, steps, warmup, gen="numpy"):
         libwkv.wkv_forward(w, u, k, v, y=y, workspace=ws)
 
     wall, per_call = time_launches(fn, steps, warmup)
-    if need:
-        assert libwkv.lookback_error(ws) == 0, "look-back gave up"
     elt = 4 if spec.dtype == "f32" else 2
     bytes_per_launch = 3 * elt * spec.elements  # read k, v; write y
+    single = per_launch_stats(fn)
+    cold = None
+    if bytes_per_launch < CACHE_FLUSH_BYTES:  # fits in the last-level cache: also time it cold
+        flush, buf = cache_flusher()
+        cold = per_launch_stats(fn, flush=flush)
+        cold["achieved_GBps_median"] = bytes_per_launch / cold["median_s"] / 1e9
+        del buf
+    if need:
+        assert libwkv.lookback_error(ws) == 0, "look-back gave up"
     out = {
         "workload": spec.name,
         "elements": spec.elements,
         "seconds": wall,
         "per_launch_s": per_call,
+        "per_launch_single": single,
         "elements_per_s": spec.elements / per_call,
         "algorithmic_bytes_per_launch": bytes_per_launch,
         "achieved_GBps": bytes_per_launch / per_call / 1e9,
         "algo": "chunked" if need else "seq",
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     del k, v, y, ws
     torch.cuda.empty_cache()
     return out
@@ -236,9 +285,16 @@ def la_case(spec, steps, warmup):
     out = torch.empty_like(v)
     need = libwkv.lib.wkv_linear_attention_workspace_bytes(spec.BH, spec.N, spec.D, spec.M, 0 if spec.dtype == "f32" else 1)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    _, per = time_launches(lambda: libwkv.linear_attention(q, k, v, out=out, workspace=ws), steps, warmup)
+    fn = lambda: libwkv.linear_attention(q, k, v, out=out, workspace=ws)  # noqa: E731
+    _, per = time_launches(fn, steps, warmup)
     elt = 4 if spec.dtype == "f32" else 2
     nbytes = spec.tokens * (2 * spec.D + 2 * spec.M) * elt  # read q, k, v; write out
+    cold = None
+    if nbytes < CACHE_FLUSH_BYTES:
+        flush, buf = cache_flusher()
+        cold = per_launch_stats(fn, flush=flush)
+        cold["achieved_GBps_median"] = nbytes / cold["median_s"] / 1e9
+        del buf
     # similarities (causal half of each 32 x 32 block), their product with v, the carried state
     # product, and the sub-chunk aggregate (counted twice: aggregate pass and output pass)
     flops = 2 * spec.tokens * (16 * spec.D + 16 * spec.M + 3 * spec.D * spec.M)
@@ -251,6 +307,8 @@ def la_case(spec, steps, warmup):
         "useful_TFLOPs": flops / per / 1e12,
         "traffic_bytes_per_call": measured_traffic(spec.name, LA_SOURCES),
     }
+    if cold is not None:
+        res["cold_cache"] = cold
     del q, k, v, out, ws
     torch.cuda.empty_cache()
     return res
@@ -292,13 +350,43 @@ def step_case(spec, steps, warmup):
     return out
 
 
-def cpu_baseline(spec, budget_s=20.0):
-    """The float64 oracle (wkv_recurrent) on a bounded sample of the workload, on the host."""
+_CPU_INPUTS = None  # the oracle sample, inherited by the forked workers of cpu_baseline
+
+
+def _oracle_slice(sl):
+    """Worker of cpu_baseline: wkv_recurrent on channels [c0, c1) of the first n_tok tokens."""
+    from oracle import wkv_recurrent
+
+    c0, c1, n_tok = sl
+    w, u, k, v = _CPU_INPUTS
+    t0 = time.perf_counter()
+    wkv_recurrent(w[c0:c1], u[c0:c1], k[:, :n_tok, c0:c1], v[:, :n_tok, c0:c1])
+    return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, budget_s=20.0, max_workers=16):
+    """The float64 oracle (wkv_recurrent) on a bounded sample of the workload, on the host:
+    one process, then the same sample split by channels over the cores this process may use
+    (at most max_workers forked processes).  Must run before anything touches the GPU (the
+    workers are forked)."""
+    import multiprocessing
+
     import numpy as np
 
     from oracle import wkv_recurrent
     from rwkv_linear_attention_libwkv_amd import workloads
 
+    global _CPU_INPUTS
     inp = workloads.forward_inputs(spec)
     # probe the cost per token, then size the sample (all lanes, leading tokens) to the budget
     t0 = time.perf_counter()
@@ -309,13 +397,28 @@ def cpu_baseline(spec, budget_s=20.0):
     wkv_recurrent(inp["w"], inp["u"], inp["k"][:, :n_tok], inp["v"][:, :n_tok])
     dt = time.perf_counter() - t0
     elements = spec.B * n_tok * spec.C
+    single = {"value": elements / dt, "unit": "elements/s", "cores": 1, "seconds": dt}
+
+    n = max(1, min(max_workers, len(os.sched_getaffinity(0)), spec.C))
+    bounds = np.linspace(0, spec.C, n + 1).astype(int)
+    slices = [(int(bounds[i]), int(bounds[i + 1]), n_tok) for i in range(n)]
+    _CPU_INPUTS = (inp["w"], inp["u"], inp["k"], inp["v"])
+    with multiprocessing.get_context("fork").Pool(n) as pool:
+        pool.map(_oracle_slice, [(0, 1, 1)] * n)  # start every worker before the clock
+        t0 = time.perf_counter()
+        pool.map(_oracle_slice, slices, chunksize=1)
+        wall = time.perf_counter() - t0
+    _CPU_INPUTS = None
     return {
-        "value": elements / dt,
+        "value": elements / wall,
         "unit": "elements/s",
-        "cores": 1,
+        "cores": n,
         "kind": "oracle",
-        "sample": f"wkv_recurrent (float64 NumPy, one process) over all {spec.B * spec.C} lanes of "
-                  f"{spec.name}, tokens 0..{n_tok - 1}: {elements} elements in {dt:.1f} s",
+        "sample": f"wkv_recurrent (float64 NumPy) over all {spec.B * spec.C} lanes of {spec.name}, tokens "
+                  f"0..{n_tok - 1} ({elements} elements): channels split over {n} forked processes, "
+                  f"{wall:.2f} s wall; one process alone {dt:.1f} s",
+        "single_process": single,
+        "cpu_model": _cpu_model(),
         "numpy": np.__version__,
     }
 
@@ -368,15 +471,24 @@ def main():
               "measures one GPU's share (see the sharding notes in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
 
+    from rwkv_linear_attention_libwkv_amd import workloads
+
+    spec = workloads.FORWARD_SPECS.get(args.workload)
+    # the oracle's baseline runs first: its workers are forked, which must happen before the
+    # GPU is initialised
+    cpu = None
+    if not (args.profile_run or args.no_cpu_baseline):
+        cpu = cpu_baseline(spec)
+        print(f"# cpu baseline: {cpu['value']:.3g} elements/s on {cpu['cores']} cores", file=sys.stderr, flush=True)
+
     import torch
 
-    from rwkv_linear_attention_libwkv_amd import libwkv, workloads  # noqa: F401  (fails loudly if unbuilt)
+    from rwkv_linear_attention_libwkv_amd import libwkv  # noqa: F401  (fails loudly if unbuilt)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile_run:
         profile_run(args.workload, max(1, min(args.steps, 5)))
         return
-    spec = workloads.FORWARD_SPECS[args.workload]
     main_res = forward_case(spec, args.steps, args.warmup)
     print(f"# {spec.name}: {main_res['per_launch_s'] * 1e6:.1f} us/launch, "
           f"{main_res['achieved_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -441,7 +553,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
         },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(spec),
+        "cpu_baseline": cpu,
         "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
