@@ -33,7 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("wkv_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h",
                   "libwkv_api.cpp")
 BACKWARD_SOURCES = KERNEL_SOURCES + ("wkv_backward.hip",)
-LA_SOURCES = ("la_forward.hip", "wkv_rows.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
+LA_SOURCES = ("la_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -283,8 +283,7 @@ def la_case(spec, steps, warmup):
     k = torch.randn((spec.BH, spec.N, spec.D), generator=g, device="cuda").to(dt)
     v = torch.randn((spec.BH, spec.N, spec.M), generator=g, device="cuda").to(dt)
     out = torch.empty_like(v)
-    need = libwkv.lib.wkv_linear_attention_workspace_bytes(spec.BH, spec.N, spec.D, spec.M, 0 if spec.dtype == "f32" else 1)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = libwkv.new_la_workspace(spec.BH, spec.N, spec.D, spec.M, dt)
     fn = lambda: libwkv.linear_attention(q, k, v, out=out, workspace=ws)  # noqa: E731
     _, per = time_launches(fn, steps, warmup)
     elt = 4 if spec.dtype == "f32" else 2
@@ -309,6 +308,7 @@ def la_case(spec, steps, warmup):
     }
     if cold is not None:
         res["cold_cache"] = cold
+    assert libwkv.lookback_error(ws) == 0, "look-back gave up"
     del q, k, v, out, ws
     torch.cuda.empty_cache()
     return res

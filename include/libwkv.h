@@ -282,9 +282,17 @@ wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
  * D = M = 32 and D = M = 64 are supported (WKV_EINVAL otherwise).  float32
  * inputs use float32 matrix cores; bfloat16 inputs use bf16 matrix cores with
  * float32 accumulation (phi, the masked similarities and the carried state
- * are rounded to bf16 as operands).  ws: device workspace of
- * wkv_linear_attention_workspace_bytes(...) bytes (no initialisation needed;
- * the call overwrites it).  Keys below about -87 underflow phi in float32.
+ * are rounded to bf16 as operands).  Chunks of positions pass their states
+ * along each sequence either by a decoupled look-back within one launch (q,
+ * k, v read once, as in the chunked WKV forward) or through a separate scan
+ * launch (see wkv_linear_attention_ex).
+ *   ws : device workspace of at least wkv_linear_attention_workspace_bytes(...)
+ *        bytes, zero-filled before its first use (wkv_forward_workspace_init)
+ *        and then owned by the library between calls: it keeps a launch
+ *        counter and per-chunk records (wkv_forward_workspace_query reports on
+ *        it as on a forward workspace).  One workspace must not be used by two
+ *        calls that may run at the same time.
+ * Keys below about -87 underflow phi in float32.
  */
 size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M,
                                             wkv_dtype dt);
@@ -293,6 +301,23 @@ wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv
                                 const void* q, const void* k, const void* v, void* out,
                                 int feature_map, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * wkv_linear_attention with the evaluation chosen: WKV_LA_ONE_PASS (one
+ * launch, chunk states passed along each sequence by look-backs), or
+ * WKV_LA_THREE_LAUNCHES (chunk aggregates, their prefix sums, outputs: q, k,
+ * v are read in the first and third launches, but no chunk waits for
+ * another, which is faster when few long sequences make the chain of
+ * look-backs the longer path).  WKV_LA_AUTO picks by the sizes (what
+ * wkv_linear_attention does).  Both give the same bits.  Another value gives
+ * WKV_EINVAL.  The workspace size is the same for every choice.
+ */
+typedef enum { WKV_LA_AUTO = 0, WKV_LA_THREE_LAUNCHES = 1, WKV_LA_ONE_PASS = 2 } wkv_la_algo;
+
+wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt,
+                                   const void* q, const void* k, const void* v, void* out,
+                                   int feature_map, void* ws, size_t ws_bytes,
+                                   wkv_la_algo algo, hipStream_t stream);
 
 /*
  * One RNN-mode decoding step for N sequences x G layer slots x C channels

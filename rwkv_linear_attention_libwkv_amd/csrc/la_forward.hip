@@ -13,15 +13,19 @@
 // inputs, v_mfma_f32_16x16x32_bf16 for bfloat16 inputs (phi, the masked similarities and the
 // entering state rounded to bf16 as operands; float32 accumulation).
 //
-// Three launches: la_chunk_kernel<0> writes each chunk's aggregate (phi(K)^T V, sum phi(K));
-// la_scan_kernel turns them, per sequence and entry, into the exclusive prefix (the state
-// entering each chunk, summed in chunk order); la_chunk_kernel<1> recomputes the sub-chunk
-// aggregates, adds them in wave order to the chunk's entering state (each workgroup thread
-// taking a slice of the entries), and writes the outputs.
-// Every sum has a fixed order, so results are bitwise reproducible.
+// One launch, one pass over q, k, v.  Chunks (workgroups) take tickets in chunk-major order.
+// A chunk sums its sub-chunk aggregates into the chunk aggregate (phi(K)^T V, sum phi(K)) and
+// publishes it; it then finds the state entering it by a decoupled look-back over the chunks
+// before it in its sequence (the plumbing of the WKV chained scan, wkv_chain.h: tagged 64-bit
+// record words, status hints, bounded waits), publishes its inclusive state, adds the sub-chunk
+// aggregates in wave order to get the state entering each wave, and writes the outputs.
+// Inclusive states follow one chain of float32 additions in chunk order (a look-back that
+// starts further back repeats the same additions), so results are bitwise reproducible and
+// equal to summing the chunk aggregates in chunk order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wkv_chain.h"
 #include "wkv_kernels.h"
 #include "wkv_rows.h"
 
@@ -141,15 +145,19 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // One region per wave holds in turn the sub-chunk's phi(K) and V rows (staged with 16-byte
 // loads, read back in the operand layouts), its aggregate phi(K)^T V (D x M) and, once every
 // wave has read the aggregates it needs, the masked similarities (32 x 32).
-template <int D, int M, int NW, int PHASE>
-struct LaShared {
+template <int D, int M, int NW>
+struct LaShared {  // (the aggregates-only phase uses the same layout)
     static constexpr int kRegion =
         cmax(kLaSub * (D + 1) + kLaSub * (M + 1), cmax(D * (M + 1), kLaSub * (kLaSub + 1)));
     float R[NW][kRegion];
-    float z[NW][D];                       // sub-chunk sums of phi(K)
-    float den[PHASE ? NW : 1][kLaSub];    // phi(q_t) . z entering the sub-chunk
+    float z[NW][D];         // sub-chunk sums of phi(K)
+    float den[NW][kLaSub];  // phi(q_t) . z entering the sub-chunk
+    int ticket;
+    int start;              // chunk the look-back folds from
     __device__ __forceinline__ float& S(int w, int d, int m) { return R[w][d * (M + 1) + m]; }
     __device__ __forceinline__ float& A(int w, int t, int c) { return R[w][t * (kLaSub + 1) + c]; }
+    // record entry e of wave w's aggregate: phi(K)^T V entries, then sum phi(K)
+    __device__ __forceinline__ float& entry(int w, int e) { return e < D * M ? S(w, e / M, e % M) : z[w][e - D * M]; }
 };
 
 // sum of x over the lanes reached by xor with lo, 2 lo, ..., hi (a butterfly)
@@ -158,18 +166,82 @@ __device__ __forceinline__ float sum_lanes(float x, int lo, int hi) {
     return x;
 }
 
-// PHASE 0: chunk aggregates into a.agg.  PHASE 1: outputs from the chunk's entering state.
+// Records of one sequence: [chunk][slot: 0 aggregate, 1 inclusive][D * M + D words].
+struct LaRecs {
+    uint64_t* rec;
+    uint32_t* status;
+    int rec_words;
+    uint32_t tag_agg, tag_incl, give_up_word;
+    __device__ __forceinline__ uint64_t* word(int chunk, int slot, int e) const {
+        return rec + ((size_t)chunk * 2 + slot) * rec_words + e;
+    }
+};
+
+// The state entering chunk ci (ci >= 1) for this thread's record entries e = threadIdx.x +
+// i * threads: wave 0 finds the nearest chunk with a published inclusive state and every chunk
+// after it published (find_inclusive); every thread then adds, to that inclusive state, the
+// aggregates of the chunks after it, in chunk order.  False after giving up.
+template <int NW, int EPT>
+__device__ __forceinline__ bool la_look_back(const LaArgs& a, const LaRecs& R, int ci, int& sh_start, int wid,
+                                             int lane, float (&pre)[EPT]) {
+    if (wid == 0) {
+        const int st = find_inclusive<-1>(R.status, a.n_chunks, ci, lane, R.tag_agg, R.tag_incl, a.ctrl,
+                                          R.give_up_word);
+        if (lane == 0) sh_start = st;
+    }
+    __syncthreads();
+    const int start = sh_start;
+    if (start < 0) return false;
+#pragma unroll 1
+    for (int c = start; c < ci; ++c) {
+        const int slot = c == start ? 1 : 0;
+        const uint32_t tag = c == start ? R.tag_incl : R.tag_agg;
+        uint64_t wv[EPT];
+        for (uint32_t spin = 0;; ++spin) {
+            bool good = true;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const int e = threadIdx.x + i * 64 * NW;
+                wv[i] = e < R.rec_words ? ld_word(R.word(c, slot, e)) : ((uint64_t)tag << 32);
+                good = good && word_tag(wv[i]) == tag;
+            }
+            if (__all(good)) break;
+            if (must_stop(a.ctrl, R.give_up_word, spin)) return raise_give_up(a.ctrl, R.give_up_word, lane);
+            __builtin_amdgcn_s_sleep(kPollSleep);
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) pre[i] = c == start ? word_val(wv[i]) : pre[i] + word_val(wv[i]);
+    }
+    return true;
+}
+
+// PHASE kAggregates: the chunk aggregates into a.agg (first of three launches).  PHASE
+// kOutputs: the outputs from the chunk's entering state, read from a.agg after la_scan_kernel
+// turned the aggregates into exclusive prefix sums (third launch).  PHASE kOnePass: both, with
+// the entering state from the look-back (one launch).
+constexpr int kAggregates = 0, kOutputs = 1, kOnePass = 2;
+
 template <typename IO, int D, int M, int NW, int PHASE>
 __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
-    constexpr int CH = kLaSub * NW;
     constexpr int ET = kLaSub / 4, ED = D / 4;  // operand elements per lane: token / feature contractions
+    constexpr int CH = kLaSub * NW;
+    constexpr int REC = D * M + D;                      // floats of a chunk state
+    constexpr int EPT = (REC + 64 * NW - 1) / (64 * NW);  // record entries per thread
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, r = lane & 15;
-    __shared__ LaShared<D, M, NW, PHASE> sh;
+    __shared__ LaShared<D, M, NW> sh;
 
-    const int bh = blockIdx.x / a.n_chunks;
-    const int ci = blockIdx.x % a.n_chunks;
+    // one pass: chunk-major tickets, so the chunks a chunk waits on hold smaller tickets and
+    // are running; otherwise the block index
+    int tile = blockIdx.x;
+    if constexpr (PHASE == kOnePass) {
+        if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&a.ctrl[kCtrlTicket], 1u);
+        __syncthreads();
+        tile = __builtin_amdgcn_readfirstlane(sh.ticket);
+    }
+    const int bh = PHASE == kOnePass ? tile % a.BH : tile / a.n_chunks;
+    const int ci = PHASE == kOnePass ? tile / a.BH : tile % a.n_chunks;
     const long t0 = (long)ci * CH + wid * kLaSub;
     const int nv = (int)max(0L, min((long)kLaSub, (long)a.N - t0));
     const long row0 = (long)bh * a.N + min(t0, (long)a.N);
@@ -198,20 +270,18 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     // phi(Q) as A (rows t, k = d; from memory: a lane's elements of a row are runs of 8
     // consecutive features, read with 16-byte loads) and phi(K) as B (k = d, columns t)
     float qa[2][ED], kb[2][ED];
-    if constexpr (PHASE == 1) {
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI) {
-            const int t = 16 * tI + r;
+    for (int tI = 0; tI < (PHASE == kAggregates ? 0 : 2); ++tI) {
+        const int t = 16 * tI + r;
 #pragma unroll
-            for (int e8 = 0; e8 < ED; e8 += 8) {
-                const int d = kidx<IO, D>(g, e8);  // first of 8 consecutive features
-                float xq[8];
-                load8<IO>(q + t * D + d, t < nv, xq);
+        for (int e8 = 0; e8 < ED; e8 += 8) {
+            const int d = kidx<IO, D>(g, e8);  // first of 8 consecutive features
+            float xq[8];
+            load8<IO>(q + t * D + d, t < nv, xq);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    qa[tI][e8 + j] = t < nv ? phi(xq[j]) : 0.f;
-                    kb[tI][e8 + j] = sk[t * (D + 1) + d + j];
-                }
+            for (int j = 0; j < 8; ++j) {
+                qa[tI][e8 + j] = t < nv ? phi(xq[j]) : 0.f;
+                kb[tI][e8 + j] = sk[t * (D + 1) + d + j];
             }
         }
     }
@@ -232,107 +302,165 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         zs = sum_lanes(zs, 16, 32);
         if (g == 0) sh.z[wid][16 * dI + r] = zs;
     }
+    __syncthreads();  // every wave's aggregate is in LDS
 
-    const size_t rec = (size_t)D * M + D;  // floats per chunk record
-    float* agg = a.agg + ((size_t)bh * a.n_chunks + ci) * rec;
-    if constexpr (PHASE == 0) {
-        __syncthreads();
-        // chunk aggregate: the sub-chunk aggregates added in wave order
-        for (int e = threadIdx.x; e < (int)rec; e += 64 * NW) {
-            float s = 0.f;
-            for (int w = 0; w < NW; ++w) s += e < D * M ? sh.S(w, e / M, e % M) : sh.z[w][e - D * M];
-            agg[e] = s;
+    // the chunk aggregate, entry by entry: the sub-chunk aggregates added in wave order
+    auto chunk_agg = [&](int e) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += sh.entry(w, e);
+        return s;
+    };
+    float* agg = a.agg + ((size_t)bh * a.n_chunks + ci) * REC;
+    if constexpr (PHASE == kAggregates) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * 64 * NW;
+            if (e < REC) agg[e] = chunk_agg(e);
         }
-    } else {
-        __syncthreads();  // every wave's aggregate is in LDS
+        return;
+    }
 
-        // ---- the state entering each wave: the chunk's plus the waves before, in wave order;
-        // the entries are split across all the workgroup's threads and replaced in place ----
-        for (int e = threadIdx.x; e < (int)rec; e += 64 * NW) {
-            float run = agg[e];
+    // ---- the state entering the chunk: the exclusive prefix in a.agg (three launches), or by
+    // the chain (one pass: publish the chunk aggregate, look back, publish the inclusive state) ----
+    float pre[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * 64 * NW;
+        pre[i] = PHASE == kOutputs && e < REC ? agg[e] : 0.f;
+    }
+    uint32_t epoch = 0;
+    if constexpr (PHASE == kOnePass) {
+        epoch = __builtin_amdgcn_readfirstlane(a.ctrl[kCtrlEpoch]);  // constant during the launch
+        LaRecs recs;
+        recs.rec = static_cast<uint64_t*>(a.recs) + (size_t)bh * a.n_chunks * 2 * REC;
+        recs.status = a.status + (size_t)bh * a.n_chunks;
+        recs.rec_words = REC;
+        recs.tag_agg = (epoch << 2) | kKindAgg;
+        recs.tag_incl = (epoch << 2) | kKindIncl;
+        recs.give_up_word = epoch | kCtrlGiveUpMark;
+        const bool has_next = ci + 1 < a.n_chunks;
+        if (ci > 0) {
+            if (has_next) {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    const int e = threadIdx.x + i * 64 * NW;
+                    if (e < REC) st_word(recs.word(ci, 0, e), chunk_agg(e), recs.tag_agg);
+                }
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&recs.status[ci], recs.tag_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (!la_look_back<NW, EPT>(a, recs, ci, sh.start, wid, lane, pre))
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) pre[i] = 0.f;
+        }
+        if (has_next) {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const int e = threadIdx.x + i * 64 * NW;
+                if (e < REC) st_word(recs.word(ci, 1, e), pre[i] + chunk_agg(e), recs.tag_incl);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&recs.status[ci], recs.tag_incl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // the state entering each wave: the chunk's plus the waves before, in wave order, replacing
+    // the sub-chunk aggregates in place
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * 64 * NW;
+        if (e < REC) {
+            float run = pre[i];
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                float& x = e < D * M ? sh.S(w, e / M, e % M) : sh.z[w][e - D * M];
+                float& x = sh.entry(w, e);
                 const float dx = x;
                 x = run;
                 run += dx;
             }
         }
-        __syncthreads();
-        float sb[M / 16][ED], zb[ED];  // as B operand (k = d, columns m)
+    }
+    __syncthreads();
+    float sb[M / 16][ED], zb[ED];  // as B operand (k = d, columns m)
 #pragma unroll
-        for (int e = 0; e < ED; ++e) {
-            const int d = kidx<IO, D>(g, e);
+    for (int e = 0; e < ED; ++e) {
+        const int d = kidx<IO, D>(g, e);
 #pragma unroll
-            for (int mJ = 0; mJ < M / 16; ++mJ) sb[mJ][e] = sh.S(wid, d, 16 * mJ + r);
-            zb[e] = sh.z[wid][d];
-        }
-        // phi(q_t) . z for the rows t = 16 tI + r
+        for (int mJ = 0; mJ < M / 16; ++mJ) sb[mJ][e] = sh.S(wid, d, 16 * mJ + r);
+        zb[e] = sh.z[wid][d];
+    }
+    // phi(q_t) . z for the rows t = 16 tI + r
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI) {
-            float p = 0.f;
+    for (int tI = 0; tI < 2; ++tI) {
+        float p = 0.f;
 #pragma unroll
-            for (int e = 0; e < ED; ++e) p = fmaf(qa[tI][e], zb[e], p);
-            p = sum_lanes(p, 16, 32);
-            if (g == 0) sh.den[wid][16 * tI + r] = p;
-        }
-        __syncthreads();  // every wave has read the aggregates: the regions take the similarities
+        for (int e = 0; e < ED; ++e) p = fmaf(qa[tI][e], zb[e], p);
+        p = sum_lanes(p, 16, 32);
+        if (g == 0) sh.den[wid][16 * tI + r] = p;
+    }
+    __syncthreads();  // every wave has read the aggregates: the regions take the similarities
 
-        // ---- masked similarities phi(Q) phi(K)^T (32 x 32) and their row sums ----
-        float rs[2][4];
+    // ---- masked similarities phi(Q) phi(K)^T (32 x 32) and their row sums ----
+    float rs[2][4];
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI) {
+    for (int tI = 0; tI < 2; ++tI) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) rs[tI][j] = 0.f;
+        for (int j = 0; j < 4; ++j) rs[tI][j] = 0.f;
 #pragma unroll
-            for (int tJ = 0; tJ < 2; ++tJ) {
-                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-                if (tJ <= tI) acc = mma<IO, D>(acc, qa[tI], kb[tJ]);
+        for (int tJ = 0; tJ < 2; ++tJ) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            if (tJ <= tI) acc = mma<IO, D>(acc, qa[tI], kb[tJ]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * tI + 4 * g + j, col = 16 * tJ + r;
-                    const float x = col <= row ? acc[j] : 0.f;
-                    sh.A(wid, row, col) = x;
-                    rs[tI][j] += x;
-                }
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tI + 4 * g + j, col = 16 * tJ + r;
+                const float x = col <= row ? acc[j] : 0.f;
+                sh.A(wid, row, col) = x;
+                rs[tI][j] += x;
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) rs[tI][j] = sum_lanes(rs[tI][j], 1, 8);
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs[tI][j] = sum_lanes(rs[tI][j], 1, 8);
+    }
+    __syncthreads();
 
-        // ---- outputs: (tril(A) V + phi(Q) S_w) / den ----
-        IO* out = static_cast<IO*>(a.out) + row0 * M;
+    // ---- outputs: (tril(A) V + phi(Q) S_w) / den ----
+    IO* out = static_cast<IO*>(a.out) + row0 * M;
 #pragma unroll
-        for (int tI = 0; tI < 2; ++tI) {
-            float aa[ET], inv[4];
+    for (int tI = 0; tI < 2; ++tI) {
+        float aa[ET], inv[4];
 #pragma unroll
-            for (int e = 0; e < ET; ++e) aa[e] = sh.A(wid, 16 * tI + r, kidx<IO, kLaSub>(g, e));
+        for (int e = 0; e < ET; ++e) aa[e] = sh.A(wid, 16 * tI + r, kidx<IO, kLaSub>(g, e));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) inv[j] = 1.f / (rs[tI][j] + sh.den[wid][16 * tI + 4 * g + j]);
+        for (int j = 0; j < 4; ++j) inv[j] = 1.f / (rs[tI][j] + sh.den[wid][16 * tI + 4 * g + j]);
 #pragma unroll
-            for (int mJ = 0; mJ < M / 16; ++mJ) {
-                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma<IO, kLaSub>(acc, aa, vb[mJ]);
-                acc = mma<IO, D>(acc, qa[tI], sb[mJ]);
+        for (int mJ = 0; mJ < M / 16; ++mJ) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma<IO, kLaSub>(acc, aa, vb[mJ]);
+            acc = mma<IO, D>(acc, qa[tI], sb[mJ]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * tI + 4 * g + j, col = 16 * mJ + r;
-                    if (row < nv) {
-                        const float y = acc[j] * inv[j];
-                        if constexpr (sizeof(IO) == 4)
-                            reinterpret_cast<float*>(out)[row * M + col] = y;
-                        else
-                            reinterpret_cast<uint16_t*>(out)[row * M + col] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
-                    }
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tI + 4 * g + j, col = 16 * mJ + r;
+                if (row < nv) {
+                    const float y = acc[j] * inv[j];
+                    if constexpr (sizeof(IO) == 4)
+                        reinterpret_cast<float*>(out)[row * M + col] = y;
+                    else
+                        reinterpret_cast<uint16_t*>(out)[row * M + col] = (uint16_t)(pack_bf16(y, 0.f) & 0xffffu);
                 }
             }
         }
     }
+
+    // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
+    if constexpr (PHASE == kOnePass) {
+        __syncthreads();
+        if (threadIdx.x == 0) finish_tile(a.ctrl, (uint32_t)a.BH * (uint32_t)a.n_chunks, epoch, false);
+    }
+    (void)CH;
 }
 
 // Per (sequence, record entry): the chunk aggregates replaced by their exclusive prefix sums,
-// in chunk order.
+// in chunk order (the second of three launches).
 __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int rec) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= (long)a.BH * rec) return;
@@ -355,10 +483,14 @@ __global__ __launch_bounds__(256) void la_scan_kernel(LaArgs a, int rec) {
 template <typename IO, int D, int M, int NW>
 static hipError_t launch_la_t(const LaArgs& a, hipStream_t s) {
     const unsigned blocks = (unsigned)((long)a.BH * a.n_chunks);
-    const int rec = D * M + D;
-    hipLaunchKernelGGL((la_chunk_kernel<IO, D, M, NW, 0>), dim3(blocks), dim3(64 * NW), 0, s, a);
-    hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)(((long)a.BH * rec + 255) / 256)), dim3(256), 0, s, a, rec);
-    hipLaunchKernelGGL((la_chunk_kernel<IO, D, M, NW, 1>), dim3(blocks), dim3(64 * NW), 0, s, a);
+    if (a.one_pass) {
+        hipLaunchKernelGGL((la_chunk_kernel<IO, D, M, NW, kOnePass>), dim3(blocks), dim3(64 * NW), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((la_chunk_kernel<IO, D, M, NW, kAggregates>), dim3(blocks), dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)(((long)a.BH * (D * M + D) + 255) / 256)), dim3(256), 0,
+                           s, a, D * M + D);
+        hipLaunchKernelGGL((la_chunk_kernel<IO, D, M, NW, kOutputs>), dim3(blocks), dim3(64 * NW), 0, s, a);
+    }
     return hipGetLastError();
 }
 

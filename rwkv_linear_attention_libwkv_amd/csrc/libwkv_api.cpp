@@ -421,20 +421,52 @@ wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const 
     return wkv::launch_token_shift(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
+// Linear-attention workspace: [control words][status word per chunk][records: per chunk, the
+// chunk's aggregate and its inclusive state, D * M + D tagged 64-bit words each] for the one-pass
+// launch, then [per chunk, D * M + D floats] for the three-launch path; a workspace serves both.
+struct LaLayout {
+    size_t off_status, off_recs, off_agg, total;
+};
+
+LaLayout la_layout(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    const size_t entries = (size_t)(BH * n_chunks) * (size_t)(D * M + D);
+    LaLayout L;
+    L.off_status = align_up((size_t)wkv::kCtrlWords * 4, kAlign);
+    L.off_recs = L.off_status + align_up((size_t)(BH * n_chunks) * 4, kAlign);
+    L.off_agg = L.off_recs + align_up(entries * 2 * 8, kAlign);
+    L.total = L.off_agg + entries * 4 + kAlign;  // + slack to align the base
+    return L;
+}
+
+// One pass unless its chain of look-backs is the longer path.  A chunk's look-back step takes
+// about 1.7 us (measured, D = M = 64, chained through a sequence), so a sequence of n chunks
+// takes at least n steps; both paths are otherwise about equally bandwidth-bound, the one pass
+// moving 1.2 and the three launches 1.6 times the algorithmic bytes (q, k, v read, out
+// written; measured 1.63 for three launches), plus about 10 us for the two extra launches.
+bool la_one_pass_auto(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
+    const double n_chunks = (double)ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    const double bytes = (double)BH * (double)N * (double)(2 * D + 2 * M) * (dt == WKV_F32 ? 4.0 : 2.0);
+    const double rate = 3.0e12;  // bytes/s either path sustains
+    const double t_one = std::max(n_chunks * 1.7e-6, 1.2 * bytes / rate);
+    const double t_three = 1.6 * bytes / rate + 10e-6;
+    return t_one <= t_three;
+}
+
 size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
     if (BH < 0 || N < 0 || !dtype_ok(dt)) return (size_t)-1;
     if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return (size_t)-1;
     if (BH == 0 || N == 0) return 0;
-    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
-    return (size_t)BH * (size_t)n_chunks * (size_t)(D * M + D) * 4 + kAlign;
+    return la_layout(BH, N, D, M).total;
 }
 
-wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt, const void* q,
-                                const void* k, const void* v, void* out, int feature_map, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt, const void* q,
+                                   const void* k, const void* v, void* out, int feature_map, void* ws,
+                                   size_t ws_bytes, wkv_la_algo algo, hipStream_t stream) {
     if (BH < 0 || N < 0 || BH > INT_MAX || N > INT_MAX) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
     if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return WKV_EINVAL;
+    if (algo != WKV_LA_AUTO && algo != WKV_LA_THREE_LAUNCHES && algo != WKV_LA_ONE_PASS) return WKV_EINVAL;
     if (BH == 0 || N == 0) return WKV_OK;
     if (!q || !k || !v || !out) return WKV_EINVAL;
     const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
@@ -446,14 +478,26 @@ wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv
     a.k = k;
     a.v = v;
     a.out = out;
-    a.agg = reinterpret_cast<float*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    const LaLayout L = la_layout(BH, N, D, M);
+    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    a.ctrl = reinterpret_cast<uint32_t*>(base);
+    a.status = reinterpret_cast<uint32_t*>(base + L.off_status);
+    a.recs = base + L.off_recs;
+    a.agg = reinterpret_cast<float*>(base + L.off_agg);
     a.BH = (int)BH;
     a.N = (int)N;
     a.D = (int)D;
     a.M = (int)M;
     a.n_chunks = (int)n_chunks;
     a.feature = feature_map ? 1 : 0;
+    a.one_pass = algo == WKV_LA_ONE_PASS || (algo == WKV_LA_AUTO && la_one_pass_auto(BH, N, D, M, dt));
     return wkv::launch_linear_attention(a, dt == WKV_F32 ? 0 : 1, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
+wkv_status wkv_linear_attention(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt, const void* q,
+                                const void* k, const void* v, void* out, int feature_map, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    return wkv_linear_attention_ex(BH, N, D, M, dt, q, k, v, out, feature_map, ws, ws_bytes, WKV_LA_AUTO, stream);
 }
 
 wkv_status wkv_step(int64_t N, int64_t G, int64_t C, wkv_dtype dt, const float* w, const float* u,

@@ -111,10 +111,16 @@ struct LaArgs {
     const void* k;
     const void* v;
     void* out;
-    float* agg;    // [BH][n_chunks][D * M + D] chunk aggregates, then their exclusive prefix
+    // one pass
+    uint32_t* ctrl;    // control block, kCtrlWords words (the chunked forward's layout)
+    uint32_t* status;  // [BH][n_chunks] status hints
+    void* recs;        // [BH][n_chunks][2][D * M + D] tagged 64-bit words: aggregate, inclusive state
+    // three launches
+    float* agg;  // [BH][n_chunks][D * M + D] chunk aggregates, then their exclusive prefix
     int BH, N, D, M;
     int n_chunks;  // ceil(N / la_chunk_len(D, M))
     int feature;   // apply phi = elu + 1 to q and k
+    int one_pass;  // one launch with look-backs, or three launches (aggregates, scan, outputs)
 };
 // Positions per chunk for these head sizes (only D = M = 32 and D = M = 64 are built).
 int la_chunk_len(int D, int M);

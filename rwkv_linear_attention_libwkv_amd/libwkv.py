@@ -39,6 +39,7 @@ EXPORTS = (
     "wkv_backward_gated",
     "wkv_linear_attention_workspace_bytes",
     "wkv_linear_attention",
+    "wkv_linear_attention_ex",
     "wkv_status_string",
 )
 
@@ -96,6 +97,8 @@ def _load() -> ctypes.CDLL:
     lib.wkv_linear_attention_workspace_bytes.restype = sz
     lib.wkv_linear_attention.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.wkv_linear_attention.restype = i32
+    lib.wkv_linear_attention_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, i32, vp]
+    lib.wkv_linear_attention_ex.restype = i32
     lib.wkv_status_string.argtypes = [i32]
     lib.wkv_status_string.restype = ctypes.c_char_p
     return lib
@@ -384,8 +387,24 @@ def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=No
     return gw, gu, gk, gv, gr
 
 
-def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, stream=None):
-    """Causal linear attention for q, k [BH, N, D] and v [BH, N, M] (float32 or bfloat16)."""
+def new_la_workspace(BH: int, N: int, D: int, M: int, dtype=torch.float32, device="cuda"):
+    """A ready (zero-filled) linear-attention workspace for these sizes, or None if none is needed.
+    It may serve any number of later calls of these sizes (one at a time)."""
+    need = lib.wkv_linear_attention_workspace_bytes(BH, N, D, M, _dtype_code(dtype))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
+    if not need:
+        return None
+    ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
+    return wkv_forward_workspace_init(ws)
+
+
+LA_ALGOS = {"auto": 0, "three": 1, "one": 2}
+
+
+def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, algo: str = "auto", stream=None):
+    """Causal linear attention for q, k [BH, N, D] and v [BH, N, M] (float32 or bfloat16).
+    algo: "one" (one launch, look-backs), "three" (aggregates, scan, outputs) or "auto"."""
     _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
           "q, k must be [BH, N, D] and v [BH, N, M]")
     _need(q.dtype == k.dtype == v.dtype and all(t.is_cuda and t.is_contiguous() for t in (q, k, v)),
@@ -398,11 +417,12 @@ def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, str
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_la_workspace(BH, N, D, M, q.dtype, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.wkv_linear_attention(BH, N, D, M, _dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                    1 if feature_map else 0, _ptr(workspace), ws_bytes, _stream(stream)),
-           "wkv_linear_attention")
+    _check(lib.wkv_linear_attention_ex(BH, N, D, M, _dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                       1 if feature_map else 0, _ptr(workspace), ws_bytes, LA_ALGOS[algo],
+                                       _stream(stream)),
+           "wkv_linear_attention_ex")
     return out
 
 

@@ -25,13 +25,19 @@ def dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(TORCH_DT[dtype])
 
 
-def run(inp, feature=True):
+ALGOS = ["one", "three"]
+
+
+def run(inp, feature=True, algo="auto"):
     d = inp["dtype"]
-    return host(libwkv.linear_attention(dev(inp["q"], d), dev(inp["k"], d), dev(inp["v"], d),
-                                        feature_map=feature))
+    q, k, v = dev(inp["q"], d), dev(inp["k"], d), dev(inp["v"], d)
+    ws = libwkv.new_la_workspace(*q.shape, v.shape[2], q.dtype)
+    out = host(libwkv.linear_attention(q, k, v, feature_map=feature, workspace=ws, algo=algo))
+    assert libwkv.lookback_error(ws) == 0
+    return out
 
 
-def check(spec, feature=True, label=""):
+def check(spec, feature=True, label="", algo="auto"):
     inp = workloads.linear_attention_inputs(spec)
     if not feature:  # positive features given directly
         inp["q"] = np.float32(elu_feature(inp["q"]))
@@ -39,28 +45,41 @@ def check(spec, feature=True, label=""):
         if spec.dtype == "bf16":
             inp["q"] = workloads.round_to_bf16(inp["q"])
             inp["k"] = workloads.round_to_bf16(inp["k"])
-    out = run(inp, feature)
+    out = run(inp, feature, algo)
     ref, scale = linear_attention_direct(inp["q"], inp["k"], inp["v"], feature=feature, return_scale=True)
     err = scaled_error(out, ref, scale)
-    print(f"  {label} {spec.name} BH={spec.BH} N={spec.N} D={spec.D} feature={feature}: {err:.2e}", flush=True)
+    print(f"  {label} {spec.name} BH={spec.BH} N={spec.N} D={spec.D} feature={feature} {algo}: {err:.2e}", flush=True)
     assert err <= TOL[spec.dtype], err
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("feature", [True, False])
-def test_small(dtype, feature):
-    check(workloads.LA_SMALL.with_(dtype=dtype, seed=1), feature)
+def test_small(dtype, feature, algo):
+    check(workloads.LA_SMALL.with_(dtype=dtype, seed=1), feature, algo=algo)
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 255, 256, 257, 600])
-def test_ragged_lengths(dtype, N):
-    check(workloads.LA_SMALL.with_(BH=3, N=N, dtype=dtype, seed=N), label="ragged")
+def test_ragged_lengths(dtype, N, algo):
+    check(workloads.LA_SMALL.with_(BH=3, N=N, dtype=dtype, seed=N), label="ragged", algo=algo)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_dim_64(dtype, algo):
+    check(workloads.LA_SMALL.with_(BH=2, N=700, D=64, M=64, dtype=dtype, seed=7), label="D=64", algo=algo)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_head_dim_64(dtype):
-    check(workloads.LA_SMALL.with_(BH=2, N=700, D=64, M=64, dtype=dtype, seed=7), label="D=64")
+@pytest.mark.parametrize("D", [32, 64])
+def test_evaluations_agree_bitwise(dtype, D):
+    """The one-pass and three-launch evaluations add the same floats in the same order."""
+    spec = workloads.LA_SMALL.with_(BH=5, N=1500, D=D, M=D, dtype=dtype, seed=3)
+    inp = workloads.linear_attention_inputs(spec)
+    one, three = run(inp, algo="one"), run(inp, algo="three")
+    assert np.array_equal(one, three)
 
 
 def test_mnist_shape():
@@ -87,10 +106,31 @@ def test_long_sequences_sampled():
 
 
 def test_deterministic():
+    """Fresh workspaces and one workspace reused by successive calls give the same bits."""
     spec = workloads.LA_CIFAR.with_(BH=8)
     inp = workloads.linear_attention_inputs(spec)
     q, k, v = (dev(inp[n], "f32") for n in ("q", "k", "v"))
     a = libwkv.linear_attention(q, k, v)
     b = libwkv.linear_attention(q, k, v)
+    ws = libwkv.new_la_workspace(spec.BH, spec.N, spec.D, spec.M, q.dtype)
+    order = ["one", "three", "one", "one", "auto"]  # the three-launch path leaves the counter alone
+    reused = [libwkv.linear_attention(q, k, v, workspace=ws, algo=al).clone() for al in order]
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    for c in reused:
+        assert torch.equal(a, c)
+    assert libwkv.lookback_error(ws) == 0 and libwkv.workspace_epoch(ws) >= 3
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_long_sequence(dtype, algo):
+    """BH = 1, N = 16384: 64 chunks chained through one sequence's look-backs, every output
+    against the cumulative-state oracle (scale from |v|, as for the sampled long case)."""
+    spec = workloads.LA_LONG.with_(BH=1, dtype=dtype, seed=11)
+    inp = workloads.linear_attention_inputs(spec)
+    out = run(inp, algo=algo)
+    ref = linear_attention_recurrent(inp["q"], inp["k"], inp["v"])
+    err = float(np.max(np.abs(out - ref))) / float(np.max(np.abs(inp["v"])))
+    print(f"  one sequence N={spec.N} {dtype} {algo}: {err:.2e}", flush=True)
+    assert err <= TOL[dtype]
