@@ -409,9 +409,34 @@ __device__ __forceinline__ void publish_rev(const RevRecs& R, int chunk, int slo
 template <int TILE>
 __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs& R, double w2, int ci, int lane,
                                               Rev& out) {
-    const int start = find_inclusive<1>(R.status, args.n_chunks, ci, lane, R.tag_agg, R.tag_incl, args.ctrl,
-                                        R.give_up_word);
-    if (start < 0) return false;
+    // every poll reads the inclusive record of chunk ci+1, which ends the search at once when
+    // complete, together with the status words of chunks ci+1 ... ci+64
+    int start;
+    for (uint32_t spin = 0;; ++spin) {
+        uint64_t inc[5];
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+            inc[q] = ld_word(R.word(ci + 1, 1, q, lane));
+            good = good && word_tag(inc[q]) == R.tag_incl;
+        }
+        const int pc = ci + 1 + lane;
+        const uint32_t st = pc < args.n_chunks ? ld_status(&R.status[pc]) : 0u;
+        if (__all(good)) {
+            out = Rev{word_val(inc[0]), word_val(inc[1]), word_val(inc[2]), word_val(inc[3]), (double)word_val(inc[4])};
+            return true;
+        }
+        start = scan_window<1>(st, pc < args.n_chunks, ci + 1, args.n_chunks - (ci + 1), R.tag_agg, R.tag_incl);
+        if (start >= 0) break;
+        if (start == kWindowAllReady) {  // 64 aggregates: continue the search beyond the window
+            start = find_inclusive<1>(R.status, args.n_chunks, ci + 64, lane, R.tag_agg, R.tag_incl, args.ctrl,
+                                      R.give_up_word);
+            if (start < 0) return false;
+            break;
+        }
+        if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
+        __builtin_amdgcn_s_sleep(kPollSleep);
+    }
     Rev P{0.f, 0.f, 0.f, 0.f, 0.0};
     bool have_p = false;
 #pragma unroll 1
@@ -498,6 +523,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
 
     BwdChunk<L> ck;
     ck.template load<IO>(rows, gyr, nv, cvalid);
+    // the forward state entering the tile, read early: wave 0 needs it right after the first
+    // barrier
+    float fwa = 0.f, fwb = 0.f, fwp = 0.f;
+    if (wid == 0) {
+        fwa = args.fw_a[ti];
+        fwb = args.fw_b[ti];
+        fwp = args.fw_p[ti];
+    }
     float sr[GATE ? L : 1];  // gate: r rows, then dL/dr
     if constexpr (GATE) BwdChunk<L>::template load_rows<IO>(rows, rows.r, cvalid && nv == L, sr);
 
@@ -530,7 +563,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     sh.p[wid][lane] = agg.p;
     __syncthreads();
     if (wid == 0) {
-        Carry run = normalize(Carry{args.fw_a[ti], args.fw_b[ti], (double)args.fw_p[ti]});
+        Carry run = normalize(Carry{fwa, fwb, (double)fwp});
 #pragma unroll 1
         for (int wv = 0; wv < NW; ++wv) {
             const int nvw = max(0, min(L, T - (t_tile + wv * L)));
@@ -567,16 +600,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     sh.r[wid][lane] = ragg.r;
     __syncthreads();
 
-    // ---- wave 0: tile aggregate, look-back, publish, carry after each wave ----
+    // ---- wave 0: the suffix aggregates (slot wv: waves wv .. NW-1), the tile aggregate (the
+    // suffix from wave 0), look-back, publish; the carry entering from the right goes to LDS ----
     if (wid == 0) {
         ck.stash(sh.stash, lane);
         asm volatile("" ::: "memory");  // the chunk must really leave the registers
+        Rev rw[NW];  // every wave's aggregate read at once (the stashed chunk's registers are free)
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv)
+            rw[wv] = Rev{sh.g[wv][lane], sh.h[wv][lane], sh.gp[wv][lane], sh.hp[wv][lane], sh.r[wv][lane]};
         Rev run = empty_rev();
-#pragma unroll 1
+#pragma unroll
         for (int wv = NW - 1; wv >= 0; --wv) {
             const int nvw = max(0, min(L, T - (t_tile + wv * L)));
-            const Rev rw{sh.g[wv][lane], sh.h[wv][lane], sh.gp[wv][lane], sh.hp[wv][lane], sh.r[wv][lane]};
-            run = normalize_rev(fold_rev(rw, run, nvw, w2));
+            run = normalize_rev(fold_rev(rw[wv], run, nvw, w2));
+            if (wv > 0) {
+                sh.g[wv][lane] = run.g;
+                sh.h[wv][lane] = run.h;
+                sh.gp[wv][lane] = run.gp;
+                sh.hp[wv][lane] = run.hp;
+                sh.r[wv][lane] = run.r;
+            }
         }
         const Rev agg_rec = rev_rec_form(run);
         Rev rin = rev_rec_form(empty_rev());
@@ -585,25 +629,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
             if (!rev_look_back<TILE>(args, recs, w2, ci, lane, rin)) rin = rev_rec_form(empty_rev());
         }
         if (ci > 0) publish_rev(recs, ci, 1, lane, advance_rev(rin, agg_rec, tile_len, w2), recs.tag_incl);
-        run = normalize_rev(rin);
-#pragma unroll 1
-        for (int wv = NW - 1; wv >= 0; --wv) {
-            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
-            const Rev rw{sh.g[wv][lane], sh.h[wv][lane], sh.gp[wv][lane], sh.hp[wv][lane], sh.r[wv][lane]};
-            sh.g[wv][lane] = run.g;  // slot wv now holds the carry after wave wv
-            sh.h[wv][lane] = run.h;
-            sh.gp[wv][lane] = run.gp;
-            sh.hp[wv][lane] = run.hp;
-            sh.r[wv][lane] = run.r;
-            run = normalize_rev(fold_rev(rw, run, nvw, w2));
-        }
+        rin = normalize_rev(rin);
+        sh.g[0][lane] = rin.g;  // slot 0 (the tile aggregate is not needed again) takes the carry
+        sh.h[0][lane] = rin.h;
+        sh.gp[0][lane] = rin.gp;
+        sh.hp[0][lane] = rin.hp;
+        sh.r[0][lane] = rin.r;
         asm volatile("" ::: "memory");
         ck.unstash(sh.stash, lane);
     }
     __syncthreads();
 
-    // ---- gradients of this wave's tokens from the carry after the wave ----
-    const Rev cin{sh.g[wid][lane], sh.h[wid][lane], sh.gp[wid][lane], sh.hp[wid][lane], sh.r[wid][lane]};
+    // ---- gradients of this wave's tokens from the carry after the wave: the carry entering
+    // the tile from the right folded through the waves after this one (their suffix aggregate)
+    Rev cin{sh.g[0][lane], sh.h[0][lane], sh.gp[0][lane], sh.hp[0][lane], sh.r[0][lane]};
+    if (wid + 1 < NW) {
+        const int n_after = max(0, min(TILE - (wid + 1) * L, T - (t_tile + (wid + 1) * L)));
+        const Rev suf{sh.g[wid + 1][lane], sh.h[wid + 1][lane], sh.gp[wid + 1][lane], sh.hp[wid + 1][lane],
+                      sh.r[wid + 1][lane]};
+        cin = normalize_rev(fold_rev(suf, cin, n_after, w2));
+    }
     if (wave_fast && __all(cin.r + (double)R <= (double)kSpanRev)) {
         ck.backward(ch, cin, R, gw, gu);
         ck.template store_grads<IO>(rows, gkr, gvr, cvalid);

@@ -55,6 +55,33 @@ __device__ __forceinline__ bool must_stop(const uint32_t* ctrl, uint32_t give_up
            __hip_atomic_load(&ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == give_up_word;
 }
 
+constexpr int kWindowWait = -1;      // no usable inclusive record in the window yet
+constexpr int kWindowAllReady = -2;  // 64 aggregates and no inclusive record: look further
+
+// One look at a window of 64 status words, lane l holding st, the status of chunk
+// nearest + DIR * l (in_range: that chunk exists; avail: chunks of the window that exist).
+// Returns the nearest chunk whose inclusive record is published while every chunk
+// between it and the window's start has published at least its aggregate, or
+// kWindowAllReady / kWindowWait.
+template <int DIR>
+__device__ __forceinline__ int scan_window(uint32_t st, bool in_range, int nearest, int avail, uint32_t tag_agg,
+                                           uint32_t tag_incl) {
+    const bool is_incl = in_range && st == tag_incl;
+    const bool is_ready = is_incl || (in_range && st == tag_agg);
+    const uint64_t incl = __ballot(is_incl);
+    const uint64_t ready = __ballot(is_ready);
+    if (incl) {
+        const int d = __builtin_ctzll(incl);
+        const uint64_t need = (d >= 63) ? ~0ull : ((2ull << d) - 1ull);
+        return (ready & need) == need ? nearest + DIR * d : kWindowWait;
+    }
+    return (avail >= 64 && ready == ~0ull) ? kWindowAllReady : kWindowWait;
+}
+
+__device__ __forceinline__ uint32_t ld_status(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The nearest chunk, going from ci in direction DIR (-1: towards chunk 0, +1: towards
 // chunk n_chunks - 1), whose inclusive record is published while every chunk between it
 // and ci has published at least its aggregate.  Lane l inspects the status word of the
@@ -70,19 +97,10 @@ __device__ __forceinline__ int find_inclusive(const uint32_t* status, int n_chun
         const bool in_range = DIR < 0 ? pc >= 0 : pc < n_chunks;
         const int avail = DIR < 0 ? nearest + 1 : n_chunks - nearest;
         for (uint32_t spin = 0;; ++spin) {
-            const uint32_t st =
-                in_range ? __hip_atomic_load(&status[pc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-            const bool is_incl = in_range && st == tag_incl;
-            const bool is_ready = is_incl || (in_range && st == tag_agg);
-            const uint64_t incl = __ballot(is_incl);
-            const uint64_t ready = __ballot(is_ready);
-            if (incl) {
-                const int d = __builtin_ctzll(incl);
-                const uint64_t need = (d >= 63) ? ~0ull : ((2ull << d) - 1ull);
-                if ((ready & need) == need) return nearest + DIR * d;
-            } else if (avail >= 64 && ready == ~0ull) {
-                break;  // 64 aggregates, no inclusive record yet: look further
-            }
+            const uint32_t st = in_range ? ld_status(&status[pc]) : 0u;
+            const int found = scan_window<DIR>(st, in_range, nearest, avail, tag_agg, tag_incl);
+            if (found >= 0) return found;
+            if (found == kWindowAllReady) break;
             if (must_stop(ctrl, give_up_word, spin)) {
                 raise_give_up(ctrl, give_up_word, lane);
                 return -1;
