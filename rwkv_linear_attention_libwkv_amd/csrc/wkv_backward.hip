@@ -362,7 +362,7 @@ __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, cons
 template <int NW>
 struct BwdShared {
     int ticket;
-    float a[NW][64];  // forward: per-wave aggregate, then the state before each wave
+    float a[NW][64];  // forward: per-wave aggregate
     float b[NW][64];
     double p[NW][64];
     float g[NW][64];  // reverse: per-wave aggregate, then the carry after each wave
@@ -523,14 +523,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
 
     BwdChunk<L> ck;
     ck.template load<IO>(rows, gyr, nv, cvalid);
-    // the forward state entering the tile, read early: wave 0 needs it right after the first
-    // barrier
-    float fwa = 0.f, fwb = 0.f, fwp = 0.f;
-    if (wid == 0) {
-        fwa = args.fw_a[ti];
-        fwb = args.fw_b[ti];
-        fwp = args.fw_p[ti];
-    }
+    // the forward state entering the tile (every wave starts its prefix from it)
+    const float fwa = args.fw_a[ti], fwb = args.fw_b[ti], fwp = args.fw_p[ti];
     float sr[GATE ? L : 1];  // gate: r rows, then dL/dr
     if constexpr (GATE) BwdChunk<L>::template load_rows<IO>(rows, rows.r, cvalid && nv == L, sr);
 
@@ -562,20 +556,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     sh.b[wid][lane] = agg.b;
     sh.p[wid][lane] = agg.p;
     __syncthreads();
-    if (wid == 0) {
-        Carry run = normalize(Carry{fwa, fwb, (double)fwp});
+    // the forward state entering this wave: the tile's state followed by the waves before it,
+    // in wave order (every wave folds its own prefix; none waits for another)
+    Carry fin = normalize(Carry{fwa, fwb, (double)fwp});
 #pragma unroll 1
-        for (int wv = 0; wv < NW; ++wv) {
-            const int nvw = max(0, min(L, T - (t_tile + wv * L)));
-            const Carry aw{sh.a[wv][lane], sh.b[wv][lane], sh.p[wv][lane]};
-            sh.a[wv][lane] = run.a;
-            sh.b[wv][lane] = run.b;
-            sh.p[wv][lane] = run.p;
-            run = normalize(combine(run, aw, (double)nvw * w2));
-        }
+    for (int wv = 0; wv < wid; ++wv) {
+        const int nvw = max(0, min(L, T - (t_tile + wv * L)));
+        const Carry aw{sh.a[wv][lane], sh.b[wv][lane], sh.p[wv][lane]};
+        fin = normalize(combine(fin, aw, (double)nvw * w2));
     }
-    __syncthreads();
-    const Carry fin = normalize(Carry{sh.a[wid][lane], sh.b[wid][lane], sh.p[wid][lane]});
 
     // ---- per-wave reverse aggregate (from nothing after the wave) ----
     const bool wave_fast = fast && __all(fin.p - (double)R <= (double)kSpan);
