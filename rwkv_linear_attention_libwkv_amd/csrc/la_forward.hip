@@ -13,15 +13,20 @@
 // inputs, v_mfma_f32_16x16x32_bf16 for bfloat16 inputs (phi, the masked similarities and the
 // entering state rounded to bf16 as operands; float32 accumulation).
 //
-// One launch, one pass over q, k, v.  Chunks (workgroups) take tickets in chunk-major order.
-// A chunk sums its sub-chunk aggregates into the chunk aggregate (phi(K)^T V, sum phi(K)) and
-// publishes it; it then finds the state entering it by a decoupled look-back over the chunks
-// before it in its sequence (the plumbing of the WKV chained scan, wkv_chain.h: tagged 64-bit
-// record words, status hints, bounded waits), publishes its inclusive state, adds the sub-chunk
-// aggregates in wave order to get the state entering each wave, and writes the outputs.
-// Inclusive states follow one chain of float32 additions in chunk order (a look-back that
-// starts further back repeats the same additions), so results are bitwise reproducible and
-// equal to summing the chunk aggregates in chunk order.
+// Chunk states along a sequence, two ways (the same floats added in the same order, so the
+// same bits):
+//  * one pass (one launch, q, k, v read once): chunks (workgroups) take tickets in chunk-major
+//    order; a chunk sums its sub-chunk aggregates into the chunk aggregate (phi(K)^T V,
+//    sum phi(K)) and publishes it, finds the state entering it by a decoupled look-back over
+//    the chunks before it in its sequence (the plumbing of the WKV chained scan, wkv_chain.h:
+//    tagged 64-bit record words, status hints, bounded waits), publishes its inclusive state,
+//    and writes its outputs.  Inclusive states follow one chain of float32 additions in chunk
+//    order (a look-back that starts further back repeats the same additions).
+//  * three launches: the chunk aggregates to memory; la_scan_kernel turns them, per sequence
+//    and entry, into exclusive prefix sums in chunk order; the outputs from those.  k and v
+//    are read twice but no chunk waits for another, which wins for few long sequences.
+// In both, the state entering each wave is the chunk's plus the earlier waves' aggregates, in
+// wave order, so results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
