@@ -102,8 +102,11 @@ wkv_status wkv_forward_workspace_init(void* ws, size_t ws_bytes, hipStream_t str
  * Diagnostics of a forward workspace, read after the calls queued on `stream`
  * have finished (this call synchronises `stream`):
  *   *gave_up : non-zero if the last chunked call on this workspace stopped
- *              waiting for a predecessor tile (its bounded spin ran out); the
- *              outputs of that call are then not valid.  Never expected.
+ *              waiting for a predecessor tile (its bounded spin ran out), or
+ *              found the workspace's launch counters in a state that only a
+ *              workspace never zero-filled (or shared by two calls at once)
+ *              leaves, in which case it wrote nothing; the outputs of that
+ *              call are then not valid.  Never expected.
  *   *epoch   : launch counter of the chunked calls made on this workspace.
  * WKV_EINVAL for NULL pointers, WKV_EWORKSPACE if ws_bytes cannot hold the
  * control block, WKV_EHIP if the synchronisation or copy fails.

@@ -244,6 +244,7 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&a.ctrl[kCtrlTicket], 1u);
         __syncthreads();
         tile = __builtin_amdgcn_readfirstlane(sh.ticket);
+        if (ticket_out_of_range((uint32_t)tile, (uint32_t)a.BH * (uint32_t)a.n_chunks, a.ctrl)) return;
     }
     const int bh = PHASE == kOnePass ? tile % a.BH : tile / a.n_chunks;
     const int ci = PHASE == kOnePass ? tile / a.BH : tile % a.n_chunks;

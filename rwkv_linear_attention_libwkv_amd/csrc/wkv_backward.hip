@@ -488,6 +488,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
     const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
+    if (ticket_out_of_range((uint32_t)ticket, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl)) return;
     const int g = ticket % args.n_groups;
     const int ci = args.n_chunks - 1 - ticket / args.n_groups;
     const int bi = g / args.groups_per_row;

@@ -111,6 +111,22 @@ __device__ __forceinline__ int find_inclusive(const uint32_t* status, int n_chun
     }
 }
 
+// A ticket past the launch's tiles only comes from a workspace that was not zero-filled
+// before its first use, or from two launches sharing one workspace at once: the workgroup
+// does nothing and flags the call.  Such a launch never completes its bookkeeping, so the
+// epoch counter stays where it was; the flag is the mark a completed launch that gave up
+// would have left (its epoch, one behind the counter), which the workspace query reports.
+// Call with a wave-uniform ticket; every thread of the workgroup gets the same answer.
+__device__ __forceinline__ bool ticket_out_of_range(uint32_t ticket, uint32_t n_tiles, uint32_t* ctrl) {
+    if (ticket < n_tiles) return false;
+    if (threadIdx.x == 0) {
+        const uint32_t epoch = __hip_atomic_load(&ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctrl[kCtrlGiveUp], ((epoch - 1u) & kCtrlEpochMask) | kCtrlGiveUpMark, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+}
+
 // End of a workgroup (one thread): count it done; the last one prepares the next launch.
 // With `inherit`, a give-up of the launch before this one (the previous epoch) is carried
 // over to this launch, so that the workspace reports it after a pair of dependent launches.

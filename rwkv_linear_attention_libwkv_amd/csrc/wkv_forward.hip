@@ -595,6 +595,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
     const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
+    if (ticket_out_of_range((uint32_t)ticket, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl)) return;
     const int g = ticket % args.n_groups;
     const int ci = ticket / args.n_groups;
     const int bi = g / args.groups_per_row;

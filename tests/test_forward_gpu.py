@@ -252,3 +252,25 @@ def test_workspace_epoch_counts_chunked_calls():
         assert libwkv.workspace_query(ws) == (0, n)
     libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="seq", workspace=ws)
     assert libwkv.workspace_query(ws) == (0, 3)
+
+
+def test_stale_ticket_counter_is_flagged():
+    """A workspace whose launch counters were not zero-filled (here: the ticket counter set past
+    every tile) makes the chunked forward flag the call and touch nothing else; zero-filling the
+    workspace again makes it usable."""
+    inp = special(B=2, T=900, C=128)
+    dev = to_device(inp)
+    k = dev["k"]
+    ws = libwkv.new_workspace(2, 900, 128, k.dtype, "chunked", 128)
+    ws.view(torch.int32)[0] = 1 << 30  # the ticket counter (first word of the control block)
+    y = torch.full_like(k, 7.0)
+    libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="chunked", chunk_len=128, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert libwkv.lookback_error(ws) == 1
+    assert bool((y == 7.0).all())
+    libwkv.wkv_forward_workspace_init(ws)
+    y = libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="chunked", chunk_len=128, workspace=ws)
+    torch.cuda.synchronize()
+    assert libwkv.lookback_error(ws) == 0
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    assert scaled_error(host(y), y_ref, s_ref) <= TOL["f32"]

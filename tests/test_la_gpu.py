@@ -134,3 +134,23 @@ def test_one_long_sequence(dtype, algo):
     err = float(np.max(np.abs(out - ref))) / float(np.max(np.abs(inp["v"])))
     print(f"  one sequence N={spec.N} {dtype} {algo}: {err:.2e}", flush=True)
     assert err <= TOL[dtype]
+
+
+def test_stale_ticket_counter_is_flagged():
+    """The one-pass evaluation with a control block that was not zero-filled (the ticket counter
+    past every chunk) flags the call and writes nothing; zero-filled again, the workspace works."""
+    spec = workloads.LA_SMALL.with_(BH=3, N=700, seed=5)
+    inp = workloads.linear_attention_inputs(spec)
+    q, k, v = (dev(inp[n], "f32") for n in ("q", "k", "v"))
+    ws = libwkv.new_la_workspace(spec.BH, spec.N, spec.D, spec.M, q.dtype)
+    ws.view(torch.int32)[0] = 1 << 30  # the ticket counter (first word of the control block)
+    out = torch.full_like(v, 7.0)
+    libwkv.linear_attention(q, k, v, out=out, workspace=ws, algo="one")
+    torch.cuda.synchronize()
+    assert libwkv.lookback_error(ws) == 1
+    assert bool((out == 7.0).all())
+    libwkv.wkv_forward_workspace_init(ws)
+    out = host(libwkv.linear_attention(q, k, v, workspace=ws, algo="one"))
+    assert libwkv.lookback_error(ws) == 0
+    ref, scale = linear_attention_direct(inp["q"], inp["k"], inp["v"], return_scale=True)
+    assert scaled_error(out, ref, scale) <= TOL["f32"]
