@@ -557,6 +557,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     sh.b[wid][lane] = agg.b;
     sh.p[wid][lane] = agg.p;
     __syncthreads();
+    // wave 0 reads the next tile's inclusive record now; by the look-back it has usually arrived
+    // complete, and the look-back is then skipped
+    const bool has_next = ci + 1 < args.n_chunks;
+    uint64_t nx[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) nx[q] = (wid == 0 && has_next) ? ld_word(recs.word(ci + 1, 1, q, lane)) : 0ull;
     // the forward state entering this wave: the tile's state followed by the waves before it,
     // in wave order (every wave folds its own prefix; none waits for another)
     Carry fin = normalize(Carry{fwa, fwb, (double)fwp});
@@ -614,9 +620,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
         }
         const Rev agg_rec = rev_rec_form(run);
         Rev rin = rev_rec_form(empty_rev());
-        if (ci + 1 < args.n_chunks) {
-            publish_rev(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-            if (!rev_look_back<TILE>(args, recs, w2, ci, lane, rin)) rin = rev_rec_form(empty_rev());
+        if (has_next) {
+            bool ready = true;
+#pragma unroll
+            for (int q = 0; q < 5; ++q) ready = ready && word_tag(nx[q]) == recs.tag_incl;
+            if (__all(ready)) {
+                rin = Rev{word_val(nx[0]), word_val(nx[1]), word_val(nx[2]), word_val(nx[3]), (double)word_val(nx[4])};
+            } else {
+                publish_rev(recs, ci, 0, lane, agg_rec, recs.tag_agg);
+                if (!rev_look_back<TILE>(args, recs, w2, ci, lane, rin)) rin = rev_rec_form(empty_rev());
+            }
         }
         if (ci > 0) publish_rev(recs, ci, 1, lane, advance_rev(rin, agg_rec, tile_len, w2), recs.tag_incl);
         rin = normalize_rev(rin);
