@@ -511,6 +511,11 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
 
     // ---- wave 0: tile aggregate, look-back, publish ----
     if (wid == 0) {
+        // the previous tile's inclusive record, read first: when it is complete, as it usually is
+        // by the time the tile has its aggregate, the look-back is skipped
+        uint64_t pv[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) pv[q] = ci > 0 ? ld_word(recs.word(ci - 1, 1, q, lane)) : 0ull;
         if constexpr (FAST) {
             chunk.stash(sh.stash, lane);
             // the chunk must really leave the registers: no forwarding of the stash
@@ -533,8 +538,15 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
             prefix = rec_form((args.sin_a && cvalid) ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
                                                       : empty_carry());
         } else {
-            publish(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-            if (!look_back<TILE, fold_batch<IO>()>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
+            bool ready = true;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) ready = ready && word_tag(pv[q]) == recs.tag_incl;
+            if (__all(ready)) {
+                prefix = Carry{word_val(pv[0]), word_val(pv[1]), (double)word_val(pv[2])};
+            } else {
+                publish(recs, ci, 0, lane, agg_rec, recs.tag_agg);
+                if (!look_back<TILE, fold_batch<IO>()>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
+            }
         }
         const Carry incl = advance(prefix, agg_rec, (double)tile_len * w2_of(ch));
         if (ci + 1 < args.n_chunks) {
