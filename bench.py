@@ -409,6 +409,15 @@ def cpu_baseline(spec, budget_s=20.0, max_workers=16):
         pool.map(_oracle_slice, slices, chunksize=1)
         wall = time.perf_counter() - t0
     _CPU_INPUTS = None
+    # the O(T^2) definition, on the smallest workload only
+    from oracle import wkv_direct
+
+    small = workloads.forward_inputs(workloads.FWD_SMALL)
+    t0 = time.perf_counter()
+    wkv_direct(small["w"], small["u"], small["k"], small["v"])
+    dt_direct = time.perf_counter() - t0
+    direct = {"value": workloads.FWD_SMALL.elements / dt_direct, "unit": "elements/s", "cores": 1,
+              "sample": f"wkv_direct (float64 NumPy, the O(T^2) definition) on {workloads.FWD_SMALL.name}"}
     return {
         "value": elements / wall,
         "unit": "elements/s",
@@ -418,6 +427,7 @@ def cpu_baseline(spec, budget_s=20.0, max_workers=16):
                   f"0..{n_tok - 1} ({elements} elements): channels split over {n} forked processes, "
                   f"{wall:.2f} s wall; one process alone {dt:.1f} s",
         "single_process": single,
+        "direct_definition": direct,
         "cpu_model": _cpu_model(),
         "numpy": np.__version__,
     }
