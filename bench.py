@@ -36,11 +36,39 @@ BACKWARD_SOURCES = KERNEL_SOURCES + ("wkv_backward.hip",)
 LA_SOURCES = ("la_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
 
 
+def strip_comments(text: str) -> str:
+    """C++ source without its comments and blank lines, each line right-trimmed, so that
+    editing a comment leaves the hash of the code unchanged."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, copied with its escapes
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = ("".join(out)).split("\n")
+    return "\n".join(l.rstrip() for l in lines if l.strip())
+
+
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for name in sources:
-        with open(os.path.join(ROOT, "rwkv_linear_attention_libwkv_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "rwkv_linear_attention_libwkv_amd", "csrc", name)) as f:
+            h.update(strip_comments(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
@@ -477,8 +505,9 @@ def main():
                          "(the byte-counter calibration), for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the WKV lanes are independent, so this build "
-              "measures one GPU's share (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the WKV lanes (batch x channel) are independent, "
+              "so each GPU of a data-parallel job runs this same kernel on its own share and the "
+              "figure to measure is one GPU's rate; pass --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     from rwkv_linear_attention_libwkv_amd import workloads

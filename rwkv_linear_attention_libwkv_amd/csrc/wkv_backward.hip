@@ -20,10 +20,11 @@
 //   1. the chunked forward kernel dumps the forward state entering every tile;
 //   2. bwd_scan_kernel, a single-pass chained scan backwards in time: per tile, recompute
 //      y and q from the dumped state, reduce the tile to its reverse aggregate (the G, H,
-//      G', H' it contributes before its start), publish it, find the reverse carry
-//      entering from the right by decoupled look-back over the later tiles, publish the
-//      inclusive carry, then walk the tokens backwards writing dL/dk, dL/dv and the
-//      tile's dL/dw, dL/du partial sums;
+//      G', H' it contributes before its start), take the reverse carry entering from the
+//      right from the next tile's inclusive record when it has already arrived, else
+//      publish the aggregate and find the carry by decoupled look-back over the later
+//      tiles, publish the inclusive carry, then walk the tokens backwards writing dL/dk,
+//      dL/dv and the tile's dL/dw, dL/du partial sums;
 //   3. bwd_reduce_kernel: per lane, sum the partials in a fixed order.
 // Every result is a deterministic function of the inputs (the carries follow one
 // canonical chain of operations whichever record a look-back starts from, and no sum

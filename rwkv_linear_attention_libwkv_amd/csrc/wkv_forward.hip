@@ -15,8 +15,9 @@
 //  * fwd_chunked_kernel: single pass over HBM.  A workgroup of NW waves owns one
 //    tile = 64 channels x (NW*L tokens); every wave keeps its L tokens of k, v in
 //    registers, reduces them to a per-wave state, the waves are combined in LDS into
-//    the tile's aggregate, and the tile's incoming state is obtained from the tiles
-//    before it by a decoupled look-back over published per-tile states (the
+//    the tile's aggregate, and the tile's incoming state is read from the previous
+//    tile's inclusive record when that has already been published, else obtained from
+//    the tiles before it by a decoupled look-back over published per-tile states (the
 //    chained-scan technique of Merrill and Garland, "Single-pass Parallel Prefix Scan
 //    with Decoupled Look-back", 2016).  Each wave then produces its outputs from its
 //    registers, so k and v are read once and y written once.
