@@ -147,20 +147,25 @@ __device__ __forceinline__ f32x4v mma(f32x4v acc, const float (&x)[K / 4], const
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Token map of the two contractions over a sub-chunk's 32 positions (phi(K)^T V and tril(A) V):
+// element e of lane group g stands for position 16 (e / 4) + 4 g + e % 4.  These are the
+// positions a lane holds as accumulator rows of the two 16-position column blocks of a
+// similarity tile computed transposed (phi(K) phi(Q)^T), so the masked similarities feed
+// tril(A) V straight from registers.  Any map that both operands share gives the same sum,
+// for the float32 and the bfloat16 MFMA shapes alike.
+__device__ __forceinline__ int tok_idx(int g, int e) { return 16 * (e / 4) + 4 * g + (e % 4); }
+
 // One region per wave holds in turn the sub-chunk's phi(K) and V rows (staged with 16-byte
-// loads, read back in the operand layouts), its aggregate phi(K)^T V (D x M) and, once every
-// wave has read the aggregates it needs, the masked similarities (32 x 32).
+// loads, read back in the operand layouts) and its aggregate phi(K)^T V (D x M).
 template <int D, int M, int NW>
 struct LaShared {  // (the aggregates-only phase uses the same layout)
-    static constexpr int kRegion =
-        cmax(kLaSub * (D + 1) + kLaSub * (M + 1), cmax(D * (M + 1), kLaSub * (kLaSub + 1)));
+    static constexpr int kRegion = cmax(kLaSub * (D + 1) + kLaSub * (M + 1), D * (M + 1));
     float R[NW][kRegion];
     float z[NW][D];         // sub-chunk sums of phi(K)
-    float den[NW][kLaSub];  // phi(q_t) . z entering the sub-chunk
+    float den[NW][kLaSub];  // the denominators: phi(q_t) . z entering the sub-chunk + row sum t
     int ticket;
     int start;              // chunk the look-back folds from
     __device__ __forceinline__ float& S(int w, int d, int m) { return R[w][d * (M + 1) + m]; }
-    __device__ __forceinline__ float& A(int w, int t, int c) { return R[w][t * (kLaSub + 1) + c]; }
     // record entry e of wave w's aggregate: phi(K)^T V entries, then sum phi(K)
     __device__ __forceinline__ float& entry(int w, int e) { return e < D * M ? S(w, e / M, e % M) : z[w][e - D * M]; }
 };
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     float ka[D / 16][ET], vb[M / 16][ET];
 #pragma unroll
     for (int e = 0; e < ET; ++e) {
-        const int t = kidx<IO, kLaSub>(g, e);
+        const int t = tok_idx(g, e);
 #pragma unroll
         for (int dI = 0; dI < D / 16; ++dI) ka[dI][e] = sk[t * (D + 1) + 16 * dI + r];
 #pragma unroll
@@ -307,6 +312,28 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         for (int e = 0; e < ET; ++e) zs += ka[dI][e];
         zs = sum_lanes(zs, 16, 32);
         if (g == 0) sh.z[wid][16 * dI + r] = zs;
+    }
+
+    // ---- masked similarities, which need no earlier chunk: tile (cJ, tI) of phi(K) phi(Q)^T
+    // leaves in lane (g, r) the entries A(t, c) = phi(q_t) . phi(k_c) for t = 16 tI + r and
+    // c = 16 cJ + 4 g + j, which are the lane's operand elements e = 4 cJ + j of row t in
+    // tril(A) V; rs[tI] is the row sum of row t ----
+    float aa[2][ET], rs[2];
+#pragma unroll
+    for (int tI = 0; tI < (PHASE == kAggregates ? 0 : 2); ++tI) {
+        float s = 0.f;
+#pragma unroll
+        for (int cJ = 0; cJ < 2; ++cJ) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            if (cJ <= tI) acc = mma<IO, D>(acc, kb[cJ], qa[tI]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = 16 * cJ + 4 * g + j <= 16 * tI + r ? acc[j] : 0.f;
+                aa[tI][4 * cJ + j] = x;
+                s += x;
+            }
+        }
+        rs[tI] = sum_lanes(s, 16, 32);
     }
     __syncthreads();  // every wave's aggregate is in LDS
 
@@ -395,53 +422,28 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         for (int mJ = 0; mJ < M / 16; ++mJ) sb[mJ][e] = sh.S(wid, d, 16 * mJ + r);
         zb[e] = sh.z[wid][d];
     }
-    // phi(q_t) . z for the rows t = 16 tI + r
+    // the denominators phi(q_t) . z + row sum for the rows t = 16 tI + r; the outputs read them
+    // back in accumulator rows (written and read by this wave only)
 #pragma unroll
     for (int tI = 0; tI < 2; ++tI) {
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < ED; ++e) p = fmaf(qa[tI][e], zb[e], p);
         p = sum_lanes(p, 16, 32);
-        if (g == 0) sh.den[wid][16 * tI + r] = p;
+        if (g == 0) sh.den[wid][16 * tI + r] = p + rs[tI];
     }
-    __syncthreads();  // every wave has read the aggregates: the regions take the similarities
-
-    // ---- masked similarities phi(Q) phi(K)^T (32 x 32) and their row sums ----
-    float rs[2][4];
-#pragma unroll
-    for (int tI = 0; tI < 2; ++tI) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rs[tI][j] = 0.f;
-#pragma unroll
-        for (int tJ = 0; tJ < 2; ++tJ) {
-            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-            if (tJ <= tI) acc = mma<IO, D>(acc, qa[tI], kb[tJ]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tI + 4 * g + j, col = 16 * tJ + r;
-                const float x = col <= row ? acc[j] : 0.f;
-                sh.A(wid, row, col) = x;
-                rs[tI][j] += x;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rs[tI][j] = sum_lanes(rs[tI][j], 1, 8);
-    }
-    __syncthreads();
 
     // ---- outputs: (tril(A) V + phi(Q) S_w) / den ----
     IO* out = static_cast<IO*>(a.out) + row0 * M;
 #pragma unroll
     for (int tI = 0; tI < 2; ++tI) {
-        float aa[ET], inv[4];
+        float inv[4];
 #pragma unroll
-        for (int e = 0; e < ET; ++e) aa[e] = sh.A(wid, 16 * tI + r, kidx<IO, kLaSub>(g, e));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) inv[j] = 1.f / (rs[tI][j] + sh.den[wid][16 * tI + 4 * g + j]);
+        for (int j = 0; j < 4; ++j) inv[j] = 1.f / sh.den[wid][16 * tI + 4 * g + j];
 #pragma unroll
         for (int mJ = 0; mJ < M / 16; ++mJ) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma<IO, kLaSub>(acc, aa, vb[mJ]);
+            acc = mma<IO, kLaSub>(acc, aa[tI], vb[mJ]);
             acc = mma<IO, D>(acc, qa[tI], sb[mJ]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
