@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "wkv_chain.h"
 #include "wkv_kernels.h"
 #include "wkv_rows.h"
@@ -79,37 +81,44 @@ __device__ __forceinline__ void load8(const IO* p, bool ok, float (&x)[8]) {
     }
 }
 
-// Rows [0, nv) of a 32 x W block (W elements per row, from src) into st[32][W + 1] as float,
-// phi applied when `feat`; rows beyond nv are zero.  Each lane moves runs of four elements
-// (16-byte float32 or 8-byte bf16 loads), so a wave reads whole rows.
+// Rows [0, nv) of a 32 x W block (W elements per row) moved through LDS: each lane loads runs
+// of four elements (16-byte float32 or 8-byte bf16 loads, so a wave reads whole rows) into
+// registers, and later stores them into st[32][W + 1] as float, phi applied when `feat`; rows
+// beyond nv are zero.
 template <typename IO, int W>
-__device__ __forceinline__ void stage_rows(const IO* src, int nv, float* st, bool feat, int lane) {
-    constexpr int VPR = W / 4;  // runs per row
+struct RowRuns {
+    static constexpr int kVpr = W / 4;                 // runs per row
+    static constexpr int kRuns = kLaSub * kVpr / 64;   // runs per lane
+    typedef typename std::conditional<sizeof(IO) == 4, f32x4a, uint32_t __attribute__((ext_vector_type(2)))>::type Run;
+    Run x[kRuns];
+
+    __device__ __forceinline__ void load(const IO* src, int nv, int lane) {
 #pragma unroll
-    for (int i = lane; i < kLaSub * VPR; i += 64) {
-        const int t = i / VPR, c = 4 * (i % VPR);
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < nv) {
-            if constexpr (sizeof(IO) == 4) {
-                const f32x4a a = *reinterpret_cast<const f32x4a*>(src + t * W + c);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = feat ? elu1(a[j]) : a[j];
-            } else {
-                typedef uint32_t u32x2a __attribute__((ext_vector_type(2)));
-                const u32x2a a = *reinterpret_cast<const u32x2a*>(src + t * W + c);
-                x[0] = bf_lo(a[0]);
-                x[1] = bf_hi(a[0]);
-                x[2] = bf_lo(a[1]);
-                x[3] = bf_hi(a[1]);
-                if (feat)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = elu1(x[j]);
-            }
+        for (int i = 0; i < kRuns; ++i) {
+            const int n = lane + 64 * i, t = n / kVpr, c = 4 * (n % kVpr);
+            x[i] = Run{};
+            if (t < nv) x[i] = *reinterpret_cast<const Run*>(src + t * W + c);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[t * (W + 1) + c + j] = x[j];
     }
-}
+    __device__ __forceinline__ void store(float* st, int nv, bool feat, int lane) const {
+#pragma unroll
+        for (int i = 0; i < kRuns; ++i) {
+            const int n = lane + 64 * i, t = n / kVpr, c = 4 * (n % kVpr);
+            float y[4];
+            if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = x[i][j];
+            } else {
+                y[0] = bf_lo(x[i][0]);
+                y[1] = bf_hi(x[i][0]);
+                y[2] = bf_lo(x[i][1]);
+                y[3] = bf_hi(x[i][1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[t * (W + 1) + c + j] = t < nv ? (feat ? elu1(y[j]) : y[j]) : 0.f;
+        }
+    }
+};
 
 // Operands of a 16 x 16 x K tile product held in registers: each lane keeps K/4 elements of
 // its A row (i = lane % 16) and of its B column (n = lane % 16).  Element e of lane group
@@ -155,11 +164,11 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // for the float32 and the bfloat16 MFMA shapes alike.
 __device__ __forceinline__ int tok_idx(int g, int e) { return 16 * (e / 4) + 4 * g + (e % 4); }
 
-// One region per wave holds in turn the sub-chunk's phi(K) and V rows (staged with 16-byte
+// One region per wave holds in turn the sub-chunk's phi(K) rows, its V rows (staged with 16-byte
 // loads, read back in the operand layouts) and its aggregate phi(K)^T V (D x M).
 template <int D, int M, int NW>
 struct LaShared {  // (the aggregates-only phase uses the same layout)
-    static constexpr int kRegion = cmax(kLaSub * (D + 1) + kLaSub * (M + 1), D * (M + 1));
+    static constexpr int kRegion = cmax(kLaSub * cmax(D + 1, M + 1), D * (M + 1));
     float R[NW][kRegion];
     float z[NW][D];         // sub-chunk sums of phi(K)
     float den[NW][kLaSub];  // the denominators: phi(q_t) . z entering the sub-chunk + row sum t
@@ -262,11 +271,16 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     const bool feat = a.feature != 0;
     auto phi = [&](float x) { return feat ? elu1(x) : x; };
 
-    // ---- stage this sub-chunk's phi(K) and V rows in the wave's region (zero beyond nv) ----
-    float* sk = sh.R[wid];                      // [32][D + 1]
-    float* sv = sh.R[wid] + kLaSub * (D + 1);   // [32][M + 1]
-    stage_rows<IO, D>(k, nv, sk, feat, lane);
-    stage_rows<IO, M>(v, nv, sv, false, lane);
+    // ---- this sub-chunk's phi(K) rows, then its V rows, pass through the wave's region (zero
+    // beyond nv) into the operand layouts; V is loaded first and stored once phi(K) is read ----
+    float* sk = sh.R[wid];  // [32][D + 1], then [32][M + 1]
+    RowRuns<IO, M> vrows;
+    vrows.load(v, nv, lane);
+    {
+        RowRuns<IO, D> krows;
+        krows.load(k, nv, lane);
+        krows.store(sk, nv, feat, lane);
+    }
 
     // ---- operands: phi(K) as A (rows d, k = t) and V as B (k = t, columns m) ----
     float ka[D / 16][ET], vb[M / 16][ET];
@@ -275,8 +289,6 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         const int t = tok_idx(g, e);
 #pragma unroll
         for (int dI = 0; dI < D / 16; ++dI) ka[dI][e] = sk[t * (D + 1) + 16 * dI + r];
-#pragma unroll
-        for (int mJ = 0; mJ < M / 16; ++mJ) vb[mJ][e] = sv[t * (M + 1) + 16 * mJ + r];
     }
     // phi(Q) as A (rows t, k = d; from memory: a lane's elements of a row are runs of 8
     // consecutive features, read with 16-byte loads) and phi(K) as B (k = d, columns t)
@@ -295,6 +307,14 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
                 kb[tI][e8 + j] = sk[t * (D + 1) + d + j];
             }
         }
+    }
+    // the region's phi(K) rows are all read (LDS accesses of a wave complete in order): V next
+    vrows.store(sk, nv, false, lane);
+#pragma unroll
+    for (int e = 0; e < ET; ++e) {
+        const int t = tok_idx(g, e);
+#pragma unroll
+        for (int mJ = 0; mJ < M / 16; ++mJ) vb[mJ][e] = sk[t * (M + 1) + 16 * mJ + r];
     }
 
     // ---- sub-chunk aggregate phi(K)^T V and sum phi(K) ----
@@ -414,14 +434,9 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         }
     }
     __syncthreads();
-    float sb[M / 16][ED], zb[ED];  // as B operand (k = d, columns m)
+    float zb[ED];  // z entering the wave as B operand (k = d)
 #pragma unroll
-    for (int e = 0; e < ED; ++e) {
-        const int d = kidx<IO, D>(g, e);
-#pragma unroll
-        for (int mJ = 0; mJ < M / 16; ++mJ) sb[mJ][e] = sh.S(wid, d, 16 * mJ + r);
-        zb[e] = sh.z[wid][d];
-    }
+    for (int e = 0; e < ED; ++e) zb[e] = sh.z[wid][kidx<IO, D>(g, e)];
     // the denominators phi(q_t) . z + row sum for the rows t = 16 tI + r; the outputs read them
     // back in accumulator rows (written and read by this wave only)
 #pragma unroll
@@ -435,21 +450,26 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
 
     // ---- outputs: (tril(A) V + phi(Q) S_w) / den ----
     IO* out = static_cast<IO*>(a.out) + row0 * M;
+    float inv[2][4];
 #pragma unroll
-    for (int tI = 0; tI < 2; ++tI) {
-        float inv[4];
+    for (int tI = 0; tI < 2; ++tI)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) inv[j] = 1.f / sh.den[wid][16 * tI + 4 * g + j];
+        for (int j = 0; j < 4; ++j) inv[tI][j] = 1.f / sh.den[wid][16 * tI + 4 * g + j];
 #pragma unroll
-        for (int mJ = 0; mJ < M / 16; ++mJ) {
+    for (int mJ = 0; mJ < M / 16; ++mJ) {
+        float sb[ED];  // S_w columns 16 mJ ... as B operand (k = d)
+#pragma unroll
+        for (int e = 0; e < ED; ++e) sb[e] = sh.S(wid, kidx<IO, D>(g, e), 16 * mJ + r);
+#pragma unroll
+        for (int tI = 0; tI < 2; ++tI) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma<IO, kLaSub>(acc, aa[tI], vb[mJ]);
-            acc = mma<IO, D>(acc, qa[tI], sb[mJ]);
+            acc = mma<IO, D>(acc, qa[tI], sb);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * tI + 4 * g + j, col = 16 * mJ + r;
                 if (row < nv) {
-                    const float y = acc[j] * inv[j];
+                    const float y = acc[j] * inv[tI][j];
                     if constexpr (sizeof(IO) == 4)
                         reinterpret_cast<float*>(out)[row * M + col] = y;
                     else
