@@ -46,39 +46,14 @@ constexpr int kLaSub = 32;  // positions per wave
 // elu(x) + 1: x + 1 for x > 0, e^x otherwise
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : ex2(x * kLog2e); }
 
-template <typename IO>
-__device__ __forceinline__ float ld(const IO* p) {
-    if constexpr (sizeof(IO) == 4)
-        return *reinterpret_cast<const float*>(p);
-    else
-        return bf_lo((uint32_t)*reinterpret_cast<const uint16_t*>(p));
-}
-
-// Eight consecutive elements (32 or 16 bytes, aligned) as floats; zeros when !ok.
 typedef float f32x4a __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
-template <typename IO>
-__device__ __forceinline__ void load8(const IO* p, bool ok, float (&x)[8]) {
-    if constexpr (sizeof(IO) == 4) {
-        f32x4a a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-        if (ok) {
-            a = *reinterpret_cast<const f32x4a*>(p);
-            b = *reinterpret_cast<const f32x4a*>(p + 4);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = a[j];
-            x[4 + j] = b[j];
-        }
-    } else {
-        u32x4a a = {0u, 0u, 0u, 0u};
-        if (ok) a = *reinterpret_cast<const u32x4a*>(p);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bf_lo(a[j]);
-            x[2 * j + 1] = bf_hi(a[j]);
-        }
-    }
+
+// A sub-chunk's rows [0, nv) of W elements as a buffer resource: loads of rows beyond nv
+// return zeros (the hardware's range check), so no load needs a branch.
+template <typename IO, int W>
+__device__ __forceinline__ Rsrc sub_chunk_rows(const IO* src, int nv) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<IO*>(src), (short)0, nv * W * (int)sizeof(IO), 0x00020000);
 }
 
 // Rows [0, nv) of a 32 x W block (W elements per row) moved through LDS: each lane loads runs
@@ -89,15 +64,20 @@ template <typename IO, int W>
 struct RowRuns {
     static constexpr int kVpr = W / 4;                 // runs per row
     static constexpr int kRuns = kLaSub * kVpr / 64;   // runs per lane
-    typedef typename std::conditional<sizeof(IO) == 4, f32x4a, uint32_t __attribute__((ext_vector_type(2)))>::type Run;
+    typedef uint32_t u32x2a __attribute__((ext_vector_type(2)));
+    typedef typename std::conditional<sizeof(IO) == 4, u32x4a, u32x2a>::type Run;
     Run x[kRuns];
 
     __device__ __forceinline__ void load(const IO* src, int nv, int lane) {
+        const Rsrc rs = sub_chunk_rows<IO, W>(src, nv);
 #pragma unroll
         for (int i = 0; i < kRuns; ++i) {
             const int n = lane + 64 * i, t = n / kVpr, c = 4 * (n % kVpr);
-            x[i] = Run{};
-            if (t < nv) x[i] = *reinterpret_cast<const Run*>(src + t * W + c);
+            const uint32_t off = (uint32_t)((t * W + c) * (int)sizeof(IO));
+            if constexpr (sizeof(IO) == 4)
+                x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
+            else
+                x[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kStream);
         }
     }
     __device__ __forceinline__ void store(float* st, int nv, bool feat, int lane) const {
@@ -107,7 +87,7 @@ struct RowRuns {
             float y[4];
             if constexpr (sizeof(IO) == 4) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = x[i][j];
+                for (int j = 0; j < 4; ++j) y[j] = __uint_as_float(x[i][j]);
             } else {
                 y[0] = bf_lo(x[i][0]);
                 y[1] = bf_hi(x[i][0]);
@@ -271,16 +251,31 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     const bool feat = a.feature != 0;
     auto phi = [&](float x) { return feat ? elu1(x) : x; };
 
-    // ---- this sub-chunk's phi(K) rows, then its V rows, pass through the wave's region (zero
-    // beyond nv) into the operand layouts; V is loaded first and stored once phi(K) is read ----
+    // ---- every load of the sub-chunk is issued first, in the order of use: K, V, Q.  The phi(K)
+    // rows, then the V rows, pass through the wave's region (zero beyond nv) into the operand
+    // layouts; Q is read in its operand layout (a lane's elements of a row are runs of 8
+    // consecutive features, 16-byte loads) ----
     float* sk = sh.R[wid];  // [32][D + 1], then [32][M + 1]
+    RowRuns<IO, D> krows;
     RowRuns<IO, M> vrows;
+    krows.load(k, nv, lane);
     vrows.load(v, nv, lane);
+    u32x4a xq[2][ED / 8][sizeof(IO) == 4 ? 2 : 1];  // raw q: 8 features per run
     {
-        RowRuns<IO, D> krows;
-        krows.load(k, nv, lane);
-        krows.store(sk, nv, feat, lane);
+        const Rsrc rq = sub_chunk_rows<IO, D>(q, nv);
+#pragma unroll
+        for (int tI = 0; tI < (PHASE == kAggregates ? 0 : 2); ++tI) {
+            const int t = 16 * tI + r;
+#pragma unroll
+            for (int e8 = 0; e8 < ED; e8 += 8) {
+                const uint32_t off = (uint32_t)((t * D + kidx<IO, D>(g, e8)) * (int)sizeof(IO));
+#pragma unroll
+                for (int h = 0; h < (sizeof(IO) == 4 ? 2 : 1); ++h)
+                    xq[tI][e8 / 8][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16 * h, 0, kStream);
+            }
+        }
     }
+    krows.store(sk, nv, feat, lane);
 
     // ---- operands: phi(K) as A (rows d, k = t) and V as B (k = t, columns m) ----
     float ka[D / 16][ET], vb[M / 16][ET];
@@ -290,8 +285,7 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
 #pragma unroll
         for (int dI = 0; dI < D / 16; ++dI) ka[dI][e] = sk[t * (D + 1) + 16 * dI + r];
     }
-    // phi(Q) as A (rows t, k = d; from memory: a lane's elements of a row are runs of 8
-    // consecutive features, read with 16-byte loads) and phi(K) as B (k = d, columns t)
+    // phi(Q) as A (rows t, k = d) and phi(K) as B (k = d, columns t)
     float qa[2][ED], kb[2][ED];
 #pragma unroll
     for (int tI = 0; tI < (PHASE == kAggregates ? 0 : 2); ++tI) {
@@ -299,11 +293,20 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
 #pragma unroll
         for (int e8 = 0; e8 < ED; e8 += 8) {
             const int d = kidx<IO, D>(g, e8);  // first of 8 consecutive features
-            float xq[8];
-            load8<IO>(q + t * D + d, t < nv, xq);
+            float x8[8];
+            if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x8[j] = __uint_as_float(xq[tI][e8 / 8][j / 4][j % 4]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x8[2 * j] = bf_lo(xq[tI][e8 / 8][0][j]);
+                    x8[2 * j + 1] = bf_hi(xq[tI][e8 / 8][0][j]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                qa[tI][e8 + j] = t < nv ? phi(xq[j]) : 0.f;
+                qa[tI][e8 + j] = t < nv ? phi(x8[j]) : 0.f;
                 kb[tI][e8 + j] = sk[t * (D + 1) + d + j];
             }
         }
