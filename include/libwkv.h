@@ -281,7 +281,8 @@ wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
  *   out_i = sum_{j<=i} phi(q_i).phi(k_j) v_j / sum_{j<=i} phi(q_i).phi(k_j),
  * with phi(x) = elu(x) + 1 applied elementwise when feature_map is non-zero,
  * and q, k used as given (they must then be positive) when it is zero.
- *   q, k : [BH, N, D], v, out : [BH, N, M], dtype dt, dense row-major.
+ *   q, k : [BH, N, D], v, out : [BH, N, M], dtype dt, dense row-major, each
+ *        16-byte aligned (rows move with 16-byte accesses; WKV_EINVAL otherwise).
  * D = M = 32 and D = M = 64 are supported (WKV_EINVAL otherwise).  float32
  * inputs use float32 matrix cores; bfloat16 inputs use bf16 matrix cores with
  * float32 accumulation (phi, the masked similarities and the carried state

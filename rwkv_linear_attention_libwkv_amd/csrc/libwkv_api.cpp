@@ -469,6 +469,8 @@ wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, 
     if (algo != WKV_LA_AUTO && algo != WKV_LA_THREE_LAUNCHES && algo != WKV_LA_ONE_PASS) return WKV_EINVAL;
     if (BH == 0 || N == 0) return WKV_OK;
     if (!q || !k || !v || !out) return WKV_EINVAL;
+    // rows are moved with 16-byte accesses
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return WKV_EINVAL;
     const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
     if (BH * n_chunks > INT_MAX || BH * N * std::max(D, M) > ((int64_t)1 << 40)) return WKV_EINVAL;
     const size_t need = wkv_linear_attention_workspace_bytes(BH, N, D, M, dt);

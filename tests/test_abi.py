@@ -228,6 +228,13 @@ def test_linear_attention_argument_checks():
     assert la(4, 100, 32, 32, F32, P, P, P, P, 1, NULL, 0, None) == EWS
     assert la(4, 100, 32, 32, F32, P, P, P, P, 1, P, need - 1, None) == EWS
     assert la(0, 100, 32, 32, F32, NULL, NULL, NULL, NULL, 1, NULL, 0, None) == OK
+    # q, k, v, out must be 16-byte aligned; checked before anything is launched
+    odd = ctypes.c_void_p(P.value + 8)
+    for i in range(4):
+        args = [P, P, P, P]
+        args[i] = odd
+        assert la(4, 100, 32, 32, BF16, *args, 1, P, need, None) == EINVAL
+        assert lx(4, 100, 32, 32, F32, *args, 1, P, need, 2, None) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
