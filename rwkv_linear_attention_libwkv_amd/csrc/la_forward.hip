@@ -27,6 +27,12 @@
 //    are read twice but no chunk waits for another, which wins for few long sequences.
 // In both, the state entering each wave is the chunk's plus the earlier waves' aggregates, in
 // wave order, so results are bitwise reproducible.
+//
+// Order of work in a wave: all of its q, k, v loads are issued first (range-checked buffer
+// loads, no branch per row); phi(K) and then V pass through the wave's LDS region into the
+// operand layouts; the sub-chunk aggregate and the masked similarities (which need no earlier
+// chunk, and stay in registers) are formed before the workgroup waits for the chunk's entering
+// state; the outputs follow.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
