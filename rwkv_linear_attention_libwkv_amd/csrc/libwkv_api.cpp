@@ -428,8 +428,8 @@ struct LaLayout {
     size_t off_status, off_recs, off_agg, total;
 };
 
-LaLayout la_layout(int64_t BH, int64_t N, int64_t D, int64_t M) {
-    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+LaLayout la_layout(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
+    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M, dt == WKV_F32 ? 0 : 1));
     const size_t entries = (size_t)(BH * n_chunks) * (size_t)(D * M + D);
     LaLayout L;
     L.off_status = align_up((size_t)wkv::kCtrlWords * 4, kAlign);
@@ -445,7 +445,7 @@ LaLayout la_layout(int64_t BH, int64_t N, int64_t D, int64_t M) {
 // moving 1.2 and the three launches 1.6 times the algorithmic bytes (q, k, v read, out
 // written; measured 1.63 for three launches), plus about 10 us for the two extra launches.
 bool la_one_pass_auto(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
-    const double n_chunks = (double)ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    const double n_chunks = (double)ceil_div(N, wkv::la_chunk_len((int)D, (int)M, dt == WKV_F32 ? 0 : 1));
     const double bytes = (double)BH * (double)N * (double)(2 * D + 2 * M) * (dt == WKV_F32 ? 4.0 : 2.0);
     const double rate = 3.0e12;  // bytes/s either path sustains
     const double t_one = std::max(n_chunks * 1.7e-6, 1.2 * bytes / rate);
@@ -457,7 +457,7 @@ size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, in
     if (BH < 0 || N < 0 || !dtype_ok(dt)) return (size_t)-1;
     if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return (size_t)-1;
     if (BH == 0 || N == 0) return 0;
-    return la_layout(BH, N, D, M).total;
+    return la_layout(BH, N, D, M, dt).total;
 }
 
 wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt, const void* q,
@@ -471,7 +471,7 @@ wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, 
     if (!q || !k || !v || !out) return WKV_EINVAL;
     // rows are moved with 16-byte accesses
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return WKV_EINVAL;
-    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M));
+    const int64_t n_chunks = ceil_div(N, wkv::la_chunk_len((int)D, (int)M, dt == WKV_F32 ? 0 : 1));
     if (BH * n_chunks > INT_MAX || BH * N * std::max(D, M) > ((int64_t)1 << 40)) return WKV_EINVAL;
     const size_t need = wkv_linear_attention_workspace_bytes(BH, N, D, M, dt);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
@@ -480,7 +480,7 @@ wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, 
     a.k = k;
     a.v = v;
     a.out = out;
-    const LaLayout L = la_layout(BH, N, D, M);
+    const LaLayout L = la_layout(BH, N, D, M, dt);
     char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
     a.ctrl = reinterpret_cast<uint32_t*>(base);
     a.status = reinterpret_cast<uint32_t*>(base + L.off_status);

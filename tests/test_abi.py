@@ -219,9 +219,11 @@ def test_linear_attention_argument_checks():
     assert lx(4, 100, 32, 32, F32, P, P, P, P, 1, P, need - 1, 2, None) == EWS
     assert lx(0, 100, 32, 32, F32, NULL, NULL, NULL, NULL, 1, NULL, 0, 1, None) == OK
     # one workspace serves both evaluations: records for the one pass and the aggregates for the
-    # three launches (per chunk of 256 positions: 2 x 1056 tagged words and 1056 floats)
+    # three launches (per chunk of 256 float32 positions, or 512 bf16 positions: 2 x 1056 tagged
+    # words and 1056 floats)
     chunks = 64 * 64
     assert q(64, 16384, 32, 32, F32) >= chunks * 1056 * (2 * 8 + 4)
+    assert q(64, 16384, 32, 32, BF16) >= chunks // 2 * 1056 * (2 * 8 + 4)
     assert la(-4, 100, 32, 32, F32, P, P, P, P, 1, P, need, None) == EINVAL
     assert la(4, 100, 32, 32, F32, NULL, P, P, P, 1, P, need, None) == EINVAL
     assert la(4, 100, 32, 32, F32, P, P, P, NULL, 1, P, need, None) == EINVAL
