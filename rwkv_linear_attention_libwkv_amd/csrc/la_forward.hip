@@ -531,16 +531,17 @@ static hipError_t launch_la_t(const LaArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Positions per chunk: 8 waves of 32 (D = M = 32, float32), 16 waves (D = M = 32, bfloat16,
+// Positions per chunk: 8 waves of 32 (D = M = 32, float32); 16 waves for D = M = 32 bfloat16,
 // whose chunk work is cheaper, so the chain of look-backs weighs more and halving its length
-// pays for the single workgroup per CU), 4 waves (D = M = 64).
-int la_chunk_len(int D, int M, int dtype) { return kLaSub * (D * M <= 1024 ? (dtype == 0 ? 8 : 16) : 4); }
+// pays for the single workgroup per CU; 8 waves for D = M = 64 (one workgroup per CU either
+// way, its LDS and registers being twice as large).
+int la_chunk_len(int D, int M, int dtype) { return kLaSub * (D * M <= 1024 ? (dtype == 0 ? 8 : 16) : 8); }
 
 hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s) {
     if (a.D == 32 && a.M == 32)
         return dtype == 0 ? launch_la_t<float, 32, 32, 8>(a, s) : launch_la_t<uint16_t, 32, 32, 16>(a, s);
     if (a.D == 64 && a.M == 64)
-        return dtype == 0 ? launch_la_t<float, 64, 64, 4>(a, s) : launch_la_t<uint16_t, 64, 64, 4>(a, s);
+        return dtype == 0 ? launch_la_t<float, 64, 64, 8>(a, s) : launch_la_t<uint16_t, 64, 64, 8>(a, s);
     return hipErrorInvalidValue;
 }
 
