@@ -77,7 +77,8 @@ typedef enum wkv_algo {
 #define WKV_P_EMPTY (-1.0e38f)
 
 /* Chunk lengths (time steps per workgroup tile) accepted by the chunked
- * algorithm; 0 selects 256 (512 for problems of fewer than 1024 tiles of 256). */
+ * algorithm; 0 selects 256 (512 for problems of fewer than 1024 tiles of 256, and
+ * for bfloat16 moved as row pairs: even C, 4-byte aligned arrays). */
 #define WKV_CHUNK_LENS {64, 128, 256, 512}
 
 /*
