@@ -62,9 +62,17 @@ def test_169m_width_workload():
 
 
 def test_bf16_io():
-    """bfloat16 k, v, y with float32 state on a shortened long-context workload."""
+    """bfloat16 k, v, y with float32 state on a shortened long-context workload (chunk 0 is the
+    default tile, 512 tokens for bfloat16 row pairs)."""
     inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(T=2048, C=512))
-    check(inp, algos=[("seq", 0), ("chunked", 128), ("chunked", 256)])
+    check(inp, algos=[("seq", 0), ("chunked", 0), ("chunked", 128), ("chunked", 256), ("chunked", 512)])
+
+
+def test_bf16_odd_width():
+    """bfloat16 with an odd C: no row pairs, one 2-byte channel per lane, at the default tile and
+    the longest one, across a ragged last tile."""
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(B=2, T=1100, C=99, seed=99))
+    check(inp, algos=[("seq", 0), ("chunked", 0), ("chunked", 512)])
 
 
 def test_bf16_output_is_rounded_float32_output():
