@@ -12,9 +12,11 @@ It evaluates what the pages define, slowly and plainly:
 * ``wkv_step_ref``    -- one RNN-mode step from a given (a, b, p) state
 * ``wkv_mp``          -- the defining sums at 50 significant digits (mpmath)
 * ``wkv_backward_direct`` -- gradients of the defining sums, O(T^2)
+* ``wkv_backward_recurrent`` -- the same gradients by forward and reverse recurrences, O(T)
 * ``token_shift``, ``token_shift_backward`` -- the time-mixing token shift (lerp of
   x_t and x_{t-1}) and its gradients
 * ``wkv_gated``, ``wkv_gated_backward`` -- the output gate sigmoid(r) * wkv and its gradients
+  (``*_recurrent``: the same from the O(T) forms, for long sequences)
 * ``linear_attention_direct``, ``linear_attention_recurrent`` -- causal linear attention
   (the linear-transformer page), masked sums and cumulative-state forms
 * ``scaled_error``    -- the scale-normalised error used as the parity gate
@@ -34,6 +36,14 @@ from .wkv_oracle import (  # noqa: F401
     state_ratio,
 )
 from .wkv_mp import wkv_mp  # noqa: F401
-from .wkv_grad import wkv_backward_direct  # noqa: F401
+from .wkv_grad import wkv_backward_direct, wkv_backward_recurrent  # noqa: F401
 from .linear_attention import elu_feature, linear_attention_direct, linear_attention_recurrent  # noqa: F401
-from .wkv_mix import sigmoid, token_shift, token_shift_backward, wkv_gated, wkv_gated_backward  # noqa: F401
+from .wkv_mix import (  # noqa: F401
+    sigmoid,
+    token_shift,
+    token_shift_backward,
+    wkv_gated,
+    wkv_gated_backward,
+    wkv_gated_backward_recurrent,
+    wkv_gated_recurrent,
+)

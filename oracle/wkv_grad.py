@@ -77,3 +77,101 @@ def wkv_backward_direct(w, u, k, v, gy, return_scale=False):
     if return_scale:
         return (gw, gu, gk, gv), (sw, su, sk, sv)
     return gw, gu, gk, gv
+
+
+def wkv_backward_recurrent(w, u, k, v, gy, return_scale=False):
+    """The same gradients as ``wkv_backward_direct`` in O(T) per lane: a forward pass for
+    the outputs and denominators, then one reverse pass over time.
+
+    With D_t = B_t + e^{u+k_t} the WKV denominator of output t (B_t the RNN-mode state of
+    section "RNN-유사추론") and q_t = gy_t / D_t, the sums over later outputs
+
+        G_i  = sum_{t>i} q_t e^{-(t-1-i) w},          H_i  = sum_{t>i} q_t y_t e^{-(t-1-i) w},
+        G'_i = sum_{t>i} (t-1-i) q_t e^{-(t-1-i) w},  H'_i = the same with q_t y_t,
+
+    obey G_{i-1} = q_i + e^{-w} G_i (H alike) and G'_{i-1} = e^{-w} (G'_i + G_i) (H' alike),
+    and the derivatives of the WKV equation are
+
+        dL/dv_i = e^{k_i} G_i + e^{u+k_i} q_i
+        dL/dk_i = e^{k_i} (v_i G_i - H_i) + e^{u+k_i} q_i (v_i - y_i)
+        dL/du   = sum_i e^{u+k_i} q_i (v_i - y_i)
+        dL/dw   = -sum_i e^{k_i} (v_i G'_i - H'_i).
+
+    The reverse sums are kept as coefficient times e^{gamma}, gamma the largest exponent
+    -(t-1-i) w - log D_t among their terms (so e^{k_i + gamma} <= 1: D_t contains the term
+    of token i).  With ``return_scale`` the same sums are formed with |gy| and magnitudes
+    (|v_i| + |y_t| for v_i - y_t): the scales ``wkv_backward_direct`` returns.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    gy = _f64(gy)
+    nb, T, C = k.shape
+    w, u = _channel_vectors(w, u, C)
+    # forward: outputs y_t and log D_t, RNN-mode state (a, b, p) with B = b e^p
+    y = np.empty((nb, T, C))
+    logd = np.empty((nb, T, C))
+    a = np.zeros((nb, C))
+    b = np.zeros((nb, C))
+    p = np.full((nb, C), -np.inf)
+    for t in range(T):
+        uk = u + k[:, t, :]
+        q = np.maximum(p, uk)
+        e_state = np.exp(p - q)
+        e_cur = np.exp(uk - q)
+        den = e_state * b + e_cur
+        y[:, t, :] = (e_state * a + e_cur * v[:, t, :]) / den
+        logd[:, t, :] = q + np.log(den)
+        pw = p - w
+        q2 = np.maximum(pw, k[:, t, :])
+        f_old = np.exp(pw - q2)
+        f_new = np.exp(k[:, t, :] - q2)
+        a = f_old * a + f_new * v[:, t, :]
+        b = f_old * b + f_new
+        p = q2
+    # reverse: (G, H, G', H') and their magnitude twins share the reference gamma
+    z = lambda: np.zeros((nb, C))  # noqa: E731
+    g, h, g1, h1 = z(), z(), z(), z()
+    ga, ha, g1a, h1a = z(), z(), z(), z()
+    gamma = np.full((nb, C), -np.inf)
+    gk = np.empty((nb, T, C))
+    gv = np.empty((nb, T, C))
+    gw = z()
+    gu = z()
+    sk = np.empty((nb, T, C))
+    sv = np.empty((nb, T, C))
+    sw = z()
+    su = z()
+    for i in range(T - 1, -1, -1):
+        ki, vi, yi, gi = k[:, i, :], v[:, i, :], y[:, i, :], gy[:, i, :]
+        # the sums over t > i are complete here
+        with np.errstate(invalid="ignore"):
+            ek = np.where(np.isneginf(gamma), 0.0, np.exp(ki + gamma))
+        cur = np.exp(u + ki - logd[:, i, :])  # e^{u+k_i} / D_i
+        gv[:, i, :] = ek * g + cur * gi
+        gk[:, i, :] = ek * (vi * g - h) + cur * gi * (vi - yi)
+        gu += cur * gi * (vi - yi)
+        gw -= ek * (vi * g1 - h1)
+        if return_scale:
+            mag = np.abs(vi) + np.abs(yi)
+            sv[:, i, :] = ek * ga + cur * np.abs(gi)
+            sk[:, i, :] = ek * (np.abs(vi) * ga + ha) + cur * np.abs(gi) * mag
+            su += cur * np.abs(gi) * mag
+            sw += ek * (np.abs(vi) * g1a + h1a)
+        # extend the sums to t > i - 1: decay the old terms by e^{-w}, add q_i
+        new = -logd[:, i, :]
+        gnext = np.maximum(gamma - w, new)
+        f_old = np.exp(gamma - w - gnext)
+        f_new = np.exp(new - gnext)
+        g1 = f_old * (g1 + g)
+        h1 = f_old * (h1 + h)
+        g = f_old * g + f_new * gi
+        h = f_old * h + f_new * gi * yi
+        if return_scale:
+            g1a = f_old * (g1a + ga)
+            h1a = f_old * (h1a + ha)
+            ga = f_old * ga + f_new * np.abs(gi)
+            ha = f_old * ha + f_new * np.abs(gi) * np.abs(yi)
+        gamma = gnext
+    if return_scale:
+        return (gw, gu, gk, gv), (sw, su, sk, sv)
+    return gw, gu, gk, gv

@@ -26,8 +26,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .wkv_oracle import _f64, wkv_direct
-from .wkv_grad import wkv_backward_direct
+from .wkv_oracle import _f64, wkv_direct, wkv_recurrent
+from .wkv_grad import wkv_backward_direct, wkv_backward_recurrent
 
 
 def sigmoid(r):
@@ -90,3 +90,24 @@ def wkv_gated_backward(w, u, k, v, r, gz, return_scale=False):
         grads, scales = wkv_backward_direct(w, u, k, v, gy, return_scale=True)
         return (*grads, gr), (*scales, np.abs(gz) * sy * s * (1.0 - s))
     return (*wkv_backward_direct(w, u, k, v, gy), gr)
+
+
+def wkv_gated_recurrent(w, u, k, v, r, return_scale=False):
+    """``wkv_gated`` with the WKV output from the O(T) RNN-mode form (long sequences)."""
+    s = sigmoid(r)
+    if return_scale:
+        y, sy = wkv_recurrent(w, u, k, v, return_scale=True)
+        return s * y, s * sy
+    return s * wkv_recurrent(w, u, k, v)
+
+
+def wkv_gated_backward_recurrent(w, u, k, v, r, gz, return_scale=False):
+    """``wkv_gated_backward`` from the O(T) forward and reverse recurrences (long sequences)."""
+    s = sigmoid(r)
+    gz = _f64(gz)
+    y, sy = wkv_recurrent(w, u, k, v, return_scale=True)
+    gr = gz * y * s * (1.0 - s)
+    if return_scale:
+        grads, scales = wkv_backward_recurrent(w, u, k, v, gz * s, return_scale=True)
+        return (*grads, gr), (*scales, np.abs(gz) * sy * s * (1.0 - s))
+    return (*wkv_backward_recurrent(w, u, k, v, gz * s), gr)

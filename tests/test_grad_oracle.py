@@ -5,11 +5,15 @@ pinned here against things it does not compute itself: central finite
 differences of the forward oracle, closed forms (T = 1, constant v), a
 conservation law (with gy = 1 the value gradients of a lane sum to T), the
 key-shift invariance of the forward, and linearity in gy.
+
+wkv_backward_recurrent reaches the same gradients through a reverse recurrence
+over time (O(T), for the long workloads).  It is pinned to the direct sums on
+ordinary and ill-conditioned inputs, and to central finite differences itself.
 """
 import numpy as np
 import pytest
 
-from oracle import wkv_backward_direct, wkv_direct
+from oracle import wkv_backward_direct, wkv_backward_recurrent, wkv_direct
 
 
 def rand_inputs(B, T, C, seed, k_std=1.0):
@@ -97,3 +101,99 @@ def test_scales_bound_the_gradients():
     grads, scales = wkv_backward_direct(w, u, k, v, gy, return_scale=True)
     for g, s in zip(grads, scales):
         assert np.all(np.abs(g) <= s * (1 + 1e-12) + 1e-300)
+
+
+def scaled_gap(a, b, s):
+    a, b, s = (np.asarray(x, dtype=np.float64) for x in (a, b, s))
+    if s.size == 0:
+        return 0.0
+    floor = 1e-300 + 2.0 ** -200 * s.max()
+    return float(np.max(np.abs(a - b) / np.maximum(s, floor)))
+
+
+def ill_conditioned(case, B=2, T=40, C=6, seed=11):
+    w, u, k, v, gy = rand_inputs(B, T, C, seed, k_std=1.5)
+    if case == "negative_w":
+        w[::2] = -0.05
+    elif case == "huge_k_range":
+        k[:, ::7, ::2] = 90.0
+        k[:, 3::11, 1::3] = -90.0
+    elif case == "huge_u":
+        u[::2] = 70.0
+    elif case == "tiny_u":
+        u[::2] = -70.0
+    elif case == "w_zero":
+        w[:] = 0.0
+    elif case == "k_plus_200":
+        k += 200.0
+    elif case == "k_minus_200":
+        k -= 200.0
+    elif case == "sparse_gy":
+        gy[:, ::3, :] = 0.0
+        gy[:, :, ::2] = 0.0
+    elif case == "huge_w":
+        w[::2] = 1000.0
+    return w, u, k, v, gy
+
+
+@pytest.mark.parametrize("B,T,C,k_std,seed", [(1, 1, 4, 1.0, 0), (2, 2, 3, 1.0, 1), (2, 9, 5, 2.0, 2),
+                                               (1, 257, 7, 2.0, 3), (3, 64, 4, 1.0, 4)])
+def test_recurrent_matches_direct(B, T, C, k_std, seed):
+    """The O(T) reverse recurrence against the term-by-term sums, gradients and scales."""
+    w, u, k, v, gy = rand_inputs(B, T, C, seed, k_std=k_std)
+    ref, ref_s = wkv_backward_direct(w, u, k, v, gy, return_scale=True)
+    got, got_s = wkv_backward_recurrent(w, u, k, v, gy, return_scale=True)
+    for name, g, r, s, gs in zip("wukv", got, ref, ref_s, got_s):
+        assert scaled_gap(g, r, s) <= 1e-12, name
+        assert scaled_gap(gs, s, s) <= 1e-12, name
+
+
+@pytest.mark.parametrize("case", ["negative_w", "huge_k_range", "huge_u", "tiny_u", "w_zero", "k_plus_200",
+                                  "k_minus_200", "sparse_gy", "huge_w"])
+def test_recurrent_matches_direct_ill_conditioned(case):
+    """Exponent ranges that overflow a plain float64 evaluation: both forms rescale exactly."""
+    w, u, k, v, gy = ill_conditioned(case)
+    ref, ref_s = wkv_backward_direct(w, u, k, v, gy, return_scale=True)
+    got, got_s = wkv_backward_recurrent(w, u, k, v, gy, return_scale=True)
+    for name, g, r, s, gs in zip("wukv", got, ref, ref_s, got_s):
+        assert np.all(np.isfinite(g)), (case, name)
+        assert scaled_gap(g, r, s) <= 1e-12, (case, name)
+        assert scaled_gap(gs, s, s) <= 1e-12, (case, name)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_recurrent_matches_central_differences(seed):
+    """The reverse recurrence against (L(x+h) - L(x-h)) / 2h of the forward's defining sums."""
+    B, T, C = 2, 7, 3
+    w, u, k, v, gy = rand_inputs(B, T, C, seed + 20, k_std=1.5)
+    gw, gu, gk, gv = wkv_backward_recurrent(w, u, k, v, gy)
+    h = 1e-6
+
+    def fd(name, idx):
+        args = {"w": w.copy(), "u": u.copy(), "k": k.copy(), "v": v.copy()}
+        args[name][idx] += h
+        lp = loss(args["w"], args["u"], args["k"], args["v"], gy)
+        args[name][idx] -= 2 * h
+        lm = loss(args["w"], args["u"], args["k"], args["v"], gy)
+        return (lp - lm) / (2 * h)
+
+    for idx in np.ndindex(B, T, C):
+        assert abs(fd("k", idx) - gk[idx]) < 1e-7, ("k", idx)
+        assert abs(fd("v", idx) - gv[idx]) < 1e-7, ("v", idx)
+    for c in range(C):
+        assert abs(fd("w", c) - gw[:, c].sum()) < 1e-7, ("w", c)
+        assert abs(fd("u", c) - gu[:, c].sum()) < 1e-7, ("u", c)
+
+
+def test_recurrent_closed_forms():
+    """T = 1 (dL/dv = gy, nothing else) and constant v (no key, bonus or decay gradient)."""
+    w, u, k, v, gy = rand_inputs(3, 1, 5, 7)
+    gw, gu, gk, gv = wkv_backward_recurrent(w, u, k, v, gy)
+    np.testing.assert_array_equal(gv, gy)
+    assert np.all(gk == 0) and np.all(gu == 0) and np.all(gw == 0)
+    w, u, k, v, gy = rand_inputs(2, 30, 4, 3, k_std=2.0)
+    v[:] = -1.25
+    gw, gu, gk, gv = wkv_backward_recurrent(w, u, k, v, gy)
+    assert np.max(np.abs(gk)) < 1e-13 and np.max(np.abs(gu)) < 1e-13 and np.max(np.abs(gw)) < 1e-12
+    _, _, _, gv = wkv_backward_recurrent(w, u, k, v, np.ones_like(v))
+    np.testing.assert_allclose(gv.sum(axis=1), 30.0, rtol=1e-13)

@@ -10,7 +10,15 @@ import pytest
 from scipy.special import expit
 
 from oracle import wkv_backward_direct, wkv_direct
-from oracle.wkv_mix import sigmoid, token_shift, token_shift_backward, wkv_gated, wkv_gated_backward
+from oracle.wkv_mix import (
+    sigmoid,
+    token_shift,
+    token_shift_backward,
+    wkv_gated,
+    wkv_gated_backward,
+    wkv_gated_backward_recurrent,
+    wkv_gated_recurrent,
+)
 
 
 def rand(shape, seed, scale=1.0):
@@ -138,3 +146,25 @@ def test_gated_scales_bound_the_gradients(seed):
     grads, scales = wkv_gated_backward(w, u, k, v, r, gz, return_scale=True)
     for g, s in zip(grads, scales):
         assert np.all(np.abs(g) <= s * (1 + 1e-12) + 1e-300)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gated_recurrent_forms_match_direct(seed):
+    """The O(T) gated forward and backward (long-sequence references) against the direct sums."""
+    rng = np.random.default_rng(seed + 40)
+    B, T, C = 2, 37, 5
+    w = np.exp(rng.uniform(-3, 1, C))
+    u = rng.normal(0, 0.5, C)
+    k = rng.normal(0, 1.5, (B, T, C))
+    v = rng.normal(0, 1, (B, T, C))
+    r = rng.normal(0, 2, (B, T, C))
+    gz = rng.normal(0, 1, (B, T, C))
+    z, sz = wkv_gated(w, u, k, v, r, return_scale=True)
+    z2, sz2 = wkv_gated_recurrent(w, u, k, v, r, return_scale=True)
+    assert np.max(np.abs(z - z2) / sz) <= 1e-12 and np.max(np.abs(sz - sz2) / sz) <= 1e-12
+    ref, ref_s = wkv_gated_backward(w, u, k, v, r, gz, return_scale=True)
+    got, got_s = wkv_gated_backward_recurrent(w, u, k, v, r, gz, return_scale=True)
+    for g, gr, s, gs in zip(got, ref, ref_s, got_s):
+        fl = 1e-300 + 2.0 ** -200 * s.max()
+        assert np.max(np.abs(g - gr) / np.maximum(s, fl)) <= 1e-12
+        assert np.max(np.abs(gs - s) / np.maximum(s, fl)) <= 1e-12
