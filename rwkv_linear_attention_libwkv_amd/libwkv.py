@@ -8,6 +8,7 @@ importing this module fails loudly when libwkv.so has not been built.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -136,6 +137,22 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with ``stream`` (when given) as torch's current stream, so that every
+    tensor it allocates (outputs, workspaces) comes from that stream's pool and is
+    zero-filled on it, ordered before the launch; the caching allocator then also
+    returns temporaries to that stream, after the launch that used them."""
+
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+
+    return wrapper
+
+
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
@@ -149,6 +166,7 @@ def wkv_forward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32, alg
     return int(n)
 
 
+@_on_stream
 def wkv_forward_workspace_init(workspace, stream=None):
     """Zero-fill a forward workspace (needed once, before its first use)."""
     _check(lib.wkv_forward_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -156,16 +174,19 @@ def wkv_forward_workspace_init(workspace, stream=None):
     return workspace
 
 
+@_on_stream
 def new_workspace(B: int, T: int, C: int, dtype=torch.float32, algo: str = "auto", chunk_len: int = 0,
-                  device="cuda"):
-    """A ready (zero-filled) workspace for these sizes, or None if none is needed."""
+                  device="cuda", stream=None):
+    """A ready (zero-filled) workspace for these sizes, or None if none is needed.  It is
+    allocated from, and zero-filled on, ``stream`` (default: torch's current stream)."""
     need = wkv_forward_workspace_bytes(B, T, C, dtype, algo, chunk_len)
     if not need:
         return None
     ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
-    return wkv_forward_workspace_init(ws)
+    return wkv_forward_workspace_init(ws, stream=stream)
 
 
+@_on_stream
 def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, workspace=None,
                 state=None, return_state: bool = False, state_out=None, stream=None):
     """y = WKV(w, u, k, v) for k, v of shape [B, T, C] (float32 or bfloat16, on the GPU).
@@ -190,7 +211,7 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
     _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
     need = wkv_forward_workspace_bytes(B, T, C, k.dtype, algo, chunk_len)
     if need and workspace is None:
-        workspace = new_workspace(B, T, C, k.dtype, algo, chunk_len, device=k.device)
+        workspace = new_workspace(B, T, C, k.dtype, algo, chunk_len, device=k.device, stream=stream)
     if workspace is not None:
         _need(workspace.is_cuda and workspace.is_contiguous(), "bad workspace")
     ws_ptr = _ptr(workspace)
@@ -219,6 +240,7 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
     return (y, sout) if return_state else y
 
 
+@_on_stream
 def wkv_step(w, u, k, v, a, b, p, *, y=None, stream=None):
     """One decoding step for k, v of shape [N, G, C]; (a, b, p) [N, G, C] float32 updated in place.
 
@@ -248,13 +270,15 @@ def wkv_backward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32) ->
     return int(n)
 
 
-def new_backward_workspace(B: int, T: int, C: int, dtype=torch.float32, device="cuda"):
-    """A ready (zero-filled) backward workspace for these sizes, or None if none is needed."""
+@_on_stream
+def new_backward_workspace(B: int, T: int, C: int, dtype=torch.float32, device="cuda", stream=None):
+    """A ready (zero-filled) backward workspace for these sizes, or None if none is needed
+    (allocated from, and zero-filled on, ``stream``)."""
     need = wkv_backward_workspace_bytes(B, T, C, dtype)
     if not need:
         return None
     ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
-    return wkv_forward_workspace_init(ws)
+    return wkv_forward_workspace_init(ws, stream=stream)
 
 
 def wkv_saved_states_bytes(B: int, T: int, C: int) -> int:
@@ -264,6 +288,7 @@ def wkv_saved_states_bytes(B: int, T: int, C: int) -> int:
     return int(n)
 
 
+@_on_stream
 def wkv_forward_save(w, u, k, v, *, y=None, saved=None, workspace=None, stream=None):
     """y = WKV(w, u, k, v) plus the states wkv_backward_saved needs: returns (y, saved).
 
@@ -281,7 +306,7 @@ def wkv_forward_save(w, u, k, v, *, y=None, saved=None, workspace=None, stream=N
         saved = torch.empty(max(4, nbytes), dtype=torch.uint8, device=k.device)
     _need(saved.is_cuda and saved.is_contiguous(), "bad saved buffer")
     if workspace is None:
-        workspace = new_workspace(B, T, C, k.dtype, "chunked", 0, device=k.device)
+        workspace = new_workspace(B, T, C, k.dtype, "chunked", 0, device=k.device, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.wkv_forward_save(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                 _ptr(saved), saved.numel() * saved.element_size(), _ptr(workspace), ws_bytes,
@@ -289,6 +314,7 @@ def wkv_forward_save(w, u, k, v, *, y=None, saved=None, workspace=None, stream=N
     return y, saved
 
 
+@_on_stream
 def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=None, workspace=None,
                  stream=None):
     """Gradients of sum(gy * WKV(w, u, k, v)): returns (gw, gu, gk, gv).
@@ -314,7 +340,7 @@ def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=No
     for t in (gw, gu):
         _need(t.numel() == B * C and t.dtype == torch.float32 and t.is_contiguous(), "bad gw or gu")
     if workspace is None:
-        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device)
+        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if saved is None:
         _check(lib.wkv_backward(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
@@ -329,6 +355,7 @@ def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=No
     return gw, gu, gk, gv
 
 
+@_on_stream
 def wkv_token_shift(x, mu, *, x_prev=None, out=None, stream=None):
     """out[m] = mu[m] * x_t + (1 - mu[m]) * x_{t-1} for x [B, T, C], mu [M, C] float32; returns [M, B, T, C]."""
     _need(x.dim() == 3 and x.is_cuda and x.is_contiguous(), "x must be a contiguous [B, T, C] GPU tensor")
@@ -345,6 +372,7 @@ def wkv_token_shift(x, mu, *, x_prev=None, out=None, stream=None):
     return out
 
 
+@_on_stream
 def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stream=None):
     """z = sigmoid(r) * WKV(w, u, k, v).  With ``saved`` (a uint8 device tensor of
     wkv_saved_states_bytes bytes) also keeps the states for wkv_backward_gated."""
@@ -358,7 +386,7 @@ def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stre
     _need(z.shape == k.shape and z.dtype == k.dtype and z.is_contiguous(), "bad z")
     algo = "chunked" if saved is not None else "auto"
     if workspace is None:
-        workspace = new_workspace(B, T, C, k.dtype, algo, 0, device=k.device)
+        workspace = new_workspace(B, T, C, k.dtype, algo, 0, device=k.device, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb = 0 if saved is None else saved.numel() * saved.element_size()
     _check(lib.wkv_forward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(z),
@@ -366,6 +394,7 @@ def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stre
     return z
 
 
+@_on_stream
 def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=None, gw=None, gu=None,
                        workspace=None, stream=None):
     """Gradients of sum(gz * sigmoid(r) * WKV(w, u, k, v)): returns (gw, gu, gk, gv, gr)."""
@@ -378,7 +407,7 @@ def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=No
     gw = torch.empty((B, C), dtype=torch.float32, device=k.device) if gw is None else gw
     gu = torch.empty((B, C), dtype=torch.float32, device=k.device) if gu is None else gu
     if workspace is None:
-        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device)
+        workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb = 0 if saved is None else saved.numel() * saved.element_size()
     _check(lib.wkv_backward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
@@ -387,21 +416,24 @@ def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=No
     return gw, gu, gk, gv, gr
 
 
-def new_la_workspace(BH: int, N: int, D: int, M: int, dtype=torch.float32, device="cuda"):
-    """A ready (zero-filled) linear-attention workspace for these sizes, or None if none is needed.
-    It may serve any number of later calls of these sizes (one at a time)."""
+@_on_stream
+def new_la_workspace(BH: int, N: int, D: int, M: int, dtype=torch.float32, device="cuda", stream=None):
+    """A ready (zero-filled) linear-attention workspace for these sizes, or None if none is needed
+    (allocated from, and zero-filled on, ``stream``).  It may serve any number of later calls of
+    these sizes (one at a time)."""
     need = lib.wkv_linear_attention_workspace_bytes(BH, N, D, M, _dtype_code(dtype))
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
     if not need:
         return None
     ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
-    return wkv_forward_workspace_init(ws)
+    return wkv_forward_workspace_init(ws, stream=stream)
 
 
 LA_ALGOS = {"auto": 0, "three": 1, "one": 2}
 
 
+@_on_stream
 def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, algo: str = "auto", stream=None):
     """Causal linear attention for q, k [BH, N, D] and v [BH, N, M] (float32 or bfloat16).
     algo: "one" (one launch, look-backs), "three" (aggregates, scan, outputs) or "auto"."""
@@ -417,7 +449,7 @@ def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, alg
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
     if workspace is None and need:
-        workspace = new_la_workspace(BH, N, D, M, q.dtype, device=q.device)
+        workspace = new_la_workspace(BH, N, D, M, q.dtype, device=q.device, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.wkv_linear_attention_ex(BH, N, D, M, _dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                        1 if feature_map else 0, _ptr(workspace), ws_bytes, LA_ALGOS[algo],
