@@ -76,6 +76,12 @@ bool sizes_ok(int64_t B, int64_t T, int64_t C) {
     return true;
 }
 
+// The scan kernels address a wave's rows through one buffer resource (2^31 - 1 bytes) with
+// 32-bit row offsets, up to kMaxRowsPerRsrc rows from its base: rows of C elements must keep
+// that window addressable.
+constexpr int64_t kMaxRowsPerRsrc = 64;
+bool rows_ok(int64_t C, wkv_dtype dt) { return C * (int64_t)dtype_size(dt) * kMaxRowsPerRsrc <= (int64_t)INT_MAX; }
+
 // States saved for the backward: 3 float32 planes (a, b, p in record form) of
 // [ceil(T / kBwdTile)][n_lanes], each plane padded to kAlign bytes.
 size_t saved_plane_bytes(int64_t B, int64_t T, int64_t C) {
@@ -90,6 +96,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
                         const void* r = nullptr) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (!rows_ok(C, dt)) return WKV_EINVAL;
     if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return WKV_EINVAL;
     if (!tile_ok(chunk_len)) return WKV_EINVAL;
     const bool in_any = sia || sib || sip, in_all = sia && sib && sip;
@@ -194,6 +201,7 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const fl
                          hipStream_t stream, const void* r = nullptr, void* gr = nullptr) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (!rows_ok(C, dt)) return WKV_EINVAL;
     if (B == 0 || C == 0) return WKV_OK;
     if (!gw || !gu) return WKV_EINVAL;
     if (T == 0) {  // no token: every gradient of w and u is zero
@@ -286,7 +294,7 @@ extern "C" {
 
 size_t wkv_forward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt, wkv_algo algo,
                                    int64_t chunk_len) {
-    if (!sizes_ok(B, T, C) || !dtype_ok(dt) || !tile_ok(chunk_len)) return (size_t)-1;
+    if (!sizes_ok(B, T, C) || !dtype_ok(dt) || !rows_ok(C, dt) || !tile_ok(chunk_len)) return (size_t)-1;
     if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SEQ && algo != WKV_ALGO_CHUNKED) return (size_t)-1;
     if (B == 0 || T == 0 || C == 0) return 0;
     if (resolve_algo(algo, B, T, C) == WKV_ALGO_SEQ) return 0;
@@ -343,7 +351,7 @@ wkv_status wkv_forward_state(int64_t B, int64_t T, int64_t C, wkv_dtype dt, cons
 }
 
 size_t wkv_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, wkv_dtype dt) {
-    if (!sizes_ok(B, T, C) || !dtype_ok(dt)) return (size_t)-1;
+    if (!sizes_ok(B, T, C) || !dtype_ok(dt) || !rows_ok(C, dt)) return (size_t)-1;
     if (B == 0 || T == 0 || C == 0) return 0;
     return backward_layout(B, T, C).total;
 }
@@ -365,6 +373,7 @@ wkv_status wkv_forward_save(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const
                             size_t ws_bytes, hipStream_t stream) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (!rows_ok(C, dt)) return WKV_EINVAL;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
     if (!saved || saved_bytes < 3 * saved_plane_bytes(B, T, C)) return WKV_EINVAL;
     return forward_impl(B, T, C, dt, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, ws,
@@ -384,6 +393,7 @@ wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt, cons
                              size_t saved_bytes, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!sizes_ok(B, T, C)) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (!rows_ok(C, dt)) return WKV_EINVAL;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
     if (!r) return WKV_EINVAL;
     if (saved && saved_bytes < 3 * saved_plane_bytes(B, T, C)) return WKV_EINVAL;

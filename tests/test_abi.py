@@ -62,6 +62,21 @@ def test_forward_argument_checks():
     assert fwd(2, 1000, 64, algo=2, ws=P, ws_bytes=need - 1) == EWS
 
 
+def test_row_window_width_limit():
+    """A wave addresses up to 64 rows from one buffer resource with 32-bit offsets: widths whose
+    64 rows pass 2^31 - 1 bytes are refused before any launch (float32 from C = 2^23, bf16 from 2^24)."""
+    assert fwd(1, 4, 1 << 23) == EINVAL
+    assert fwd(1, 4, 1 << 24, dt=BF16) == EINVAL
+    # the widest accepted widths still get a workspace size (queries launch nothing)
+    assert lib.wkv_forward_workspace_bytes(1, 4096, (1 << 23) - 1, F32, 2, 0) > 0
+    assert lib.wkv_forward_workspace_bytes(1, 4096, (1 << 24) - 1, BF16, 2, 0) > 0
+    assert lib.wkv_forward_workspace_bytes(1, 4096, 1 << 23, F32, 2, 0) == ctypes.c_size_t(-1).value
+    assert lib.wkv_forward_workspace_bytes(1, 4096, 1 << 24, BF16, 2, 0) == ctypes.c_size_t(-1).value
+    assert lib.wkv_backward_workspace_bytes(1, 4096, 1 << 23, F32) == ctypes.c_size_t(-1).value
+    assert lib.wkv_backward(1, 4, 1 << 23, F32, P, P, P, P, P, P, P, P, P, P, 1 << 20, None) == EINVAL
+    assert lib.wkv_forward_gated(1, 4, 1 << 24, BF16, P, P, P, P, P, P, NULL, 0, P, 1 << 20, None) == EINVAL
+
+
 def test_forward_empty_problems_are_noops():
     for B, T, C in [(0, 5, 5), (5, 0, 5), (5, 5, 0)]:
         assert fwd(B, T, C, w=NULL, u=NULL, k=NULL, v=NULL, y=NULL) == OK
