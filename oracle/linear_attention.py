@@ -52,18 +52,27 @@ def linear_attention_direct(q, k, v, feature=True, return_scale=False):
     return out
 
 
-def linear_attention_recurrent(q, k, v, feature=True):
-    """The same outputs from the states S_i (D x M) and Z_i (D), one step per position."""
+def linear_attention_recurrent(q, k, v, feature=True, return_scale=False):
+    """The same outputs from the states S_i (D x M) and Z_i (D), one step per position.
+
+    With ``return_scale`` a third state, the same cumulative sum of phi(K_j) |V_j|^T, gives
+    the scale (the normalised sum applied to |v|, as ``linear_attention_direct`` returns it)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     fq = elu_feature(q) if feature else q
     fk = elu_feature(k) if feature else k
     bh, n, d = q.shape
     m = v.shape[2]
     s = np.zeros((bh, d, m))
+    s_abs = np.zeros((bh, d, m)) if return_scale else None
     z = np.zeros((bh, d))
     out = np.empty((bh, n, m))
+    scale = np.empty((bh, n, m)) if return_scale else None
     for i in range(n):
         s += fk[:, i, :, None] * v[:, i, None, :]
         z += fk[:, i, :]
-        out[:, i, :] = np.einsum("bd,bdm->bm", fq[:, i, :], s) / np.einsum("bd,bd->b", fq[:, i, :], z)[:, None]
-    return out
+        den = np.einsum("bd,bd->b", fq[:, i, :], z)[:, None]
+        out[:, i, :] = np.einsum("bd,bdm->bm", fq[:, i, :], s) / den
+        if return_scale:
+            s_abs += fk[:, i, :, None] * np.abs(v[:, i, None, :])
+            scale[:, i, :] = np.einsum("bd,bdm->bm", fq[:, i, :], s_abs) / den
+    return (out, scale) if return_scale else out

@@ -50,6 +50,21 @@ def test_direct_matches_recurrent(shape):
                                rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("shape", [(2, 9, 4, 3), (1, 40, 8, 8)])
+def test_recurrent_scale_matches_direct(shape):
+    """The cumulative |v| state gives the direct form's scale; the scale bounds |out| and equals
+    |out| when every value has one sign."""
+    bh, n, d, m = shape
+    q, k, v = rand((bh, n, d), 4), rand((bh, n, d), 5), rand((bh, n, m), 6)
+    out_d, sc_d = linear_attention_direct(q, k, v, return_scale=True)
+    out_r, sc_r = linear_attention_recurrent(q, k, v, return_scale=True)
+    np.testing.assert_allclose(out_r, out_d, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sc_r, sc_d, rtol=1e-12, atol=0)
+    assert np.all(np.abs(out_r) <= sc_r * (1 + 1e-12))
+    _, sc_pos = linear_attention_recurrent(q, k, np.abs(v), return_scale=True)
+    np.testing.assert_allclose(sc_pos, linear_attention_recurrent(q, k, np.abs(v)), rtol=1e-12)
+
+
 def test_one_dimension_is_wkv_without_decay_or_bonus():
     """D = 1 with phi(k) = e^k and any positive query is sum_{j<=i} e^{k_j} v_j / sum e^{k_j}:
     the WKV equation at w = 0, u = 0, one channel per value column."""
