@@ -36,6 +36,9 @@
  *    WKV_OK without touching the GPU.
  *  - y must not alias k or v (not detected).  NaN and Inf in the inputs
  *    propagate to the outputs; nothing traps.
+ *  - The scan kernels address up to 64 rows of C elements from one 32-bit
+ *    window: C * (bytes per element) * 64 must not exceed 2^31 - 1 (C below
+ *    2^23 for float32, 2^24 for bfloat16); wider rows give WKV_EINVAL.
  *  - Results are bitwise reproducible for a given shape, dtype, algorithm
  *    and chunk length.
  */
@@ -102,18 +105,33 @@ wkv_status wkv_forward_workspace_init(void* ws, size_t ws_bytes, hipStream_t str
 /*
  * Diagnostics of a forward workspace, read after the calls queued on `stream`
  * have finished (this call synchronises `stream`):
- *   *gave_up : non-zero if the last chunked call on this workspace stopped
- *              waiting for a predecessor tile (its bounded spin ran out), or
- *              found the workspace's launch counters in a state that only a
- *              workspace never zero-filled (or shared by two calls at once)
- *              leaves, in which case it wrote nothing; the outputs of that
- *              call are then not valid.  Never expected.
+ *   *gave_up : non-zero if the last chunked call on this workspace had a tile
+ *              stop waiting for another (its bounded spin ran out, another tile
+ *              of the call had stopped, the call was forced onto that path by
+ *              wkv_workspace_force_give_up, or the workspace's ticket counter
+ *              was not zero when the call started).  Such a tile rebuilds the
+ *              state it needs without waiting (from the complete records and
+ *              the inputs in memory), so the outputs stay valid; the flag only
+ *              says that the slower path ran.
  *   *epoch   : launch counter of the chunked calls made on this workspace.
  * WKV_EINVAL for NULL pointers, WKV_EWORKSPACE if ws_bytes cannot hold the
  * control block, WKV_EHIP if the synchronisation or copy fails.
  */
 wkv_status wkv_forward_workspace_query(const void* ws, size_t ws_bytes, uint32_t* gave_up,
                                        uint32_t* epoch, hipStream_t stream);
+
+/*
+ * Test hook of the give-up path of the chained scans (wkv_forward*,
+ * wkv_backward*, wkv_linear_attention* in one pass): the next `launches`
+ * chained-scan launches on this workspace (a recomputing wkv_backward makes
+ * two) run every tile as if each of its waits had given up at once, so every
+ * tile rebuilds its entering state from the complete records and the inputs
+ * in memory.  Results stay within the stated tolerances (they are no longer
+ * bitwise those of the usual path), and the calls are slower.  Asynchronous
+ * on `stream`, no allocation.  ws as for wkv_forward_workspace_query
+ * (WKV_EINVAL for NULL, WKV_EWORKSPACE if it cannot hold the control block).
+ */
+wkv_status wkv_workspace_force_give_up(void* ws, size_t ws_bytes, uint32_t launches, hipStream_t stream);
 
 /*
  * Whole-sequence WKV (the page's time-parallel training mode, section

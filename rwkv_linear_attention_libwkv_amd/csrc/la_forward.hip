@@ -220,6 +220,62 @@ __device__ __forceinline__ bool la_look_back(const LaArgs& a, const LaRecs& R, i
     return true;
 }
 
+// An element of q, k or v as float32.
+template <typename IO>
+__device__ __forceinline__ float la_elt(const IO* p, size_t i) {
+    if constexpr (sizeof(IO) == 4)
+        return reinterpret_cast<const float*>(p)[i];
+    else
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+}
+
+// The state entering chunk ci for this thread's record entries without waiting on any other
+// chunk, for a chunk whose look-back gave up or a launch forced onto that path.  The entries
+// are independent sums over the chunks before ci, so each thread rebuilds its own: walking
+// back from chunk ci - 1, it stops at the first complete inclusive word of its entry (or at
+// the sequence start), adding on the way each complete aggregate word, and, for a chunk whose
+// word is missing, that chunk's entry summed again from k and v in memory (phi(k_j)[d] v_j[m],
+// or phi(k_j)[d] for the sum of phi(K)).  Every word used is validated by its own tag.
+template <typename IO, int D, int M, int NW, int EPT>
+__device__ __forceinline__ void la_rebuild(const LaArgs& a, const LaRecs& R, int bh, int ci, int chunk_len,
+                                           float (&pre)[EPT]) {
+    constexpr int REC = D * M + D;
+    const bool feat = a.feature != 0;
+    const IO* k = static_cast<const IO*>(a.k) + (size_t)bh * a.N * D;
+    const IO* v = static_cast<const IO*>(a.v) + (size_t)bh * a.N * M;
+#pragma unroll 1
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * 64 * NW;
+        float acc = 0.f;
+        if (e < REC) {
+            const int d = e < D * M ? e / M : e - D * M, m = e % M;
+#pragma unroll 1
+            for (int c = ci - 1; c >= 0; --c) {
+                const uint64_t wi = ld_word(R.word(c, 1, e));
+                if (word_tag(wi) == R.tag_incl) {
+                    acc += word_val(wi);
+                    break;
+                }
+                const uint64_t wa = ld_word(R.word(c, 0, e));
+                if (word_tag(wa) == R.tag_agg) {
+                    acc += word_val(wa);
+                    continue;
+                }
+                const int r0 = c * chunk_len, n = min(chunk_len, a.N - r0);
+                float sum = 0.f;
+#pragma unroll 1
+                for (int j = 0; j < n; ++j) {
+                    const float kf = la_elt(k, (size_t)(r0 + j) * D + d);
+                    const float ph = feat ? elu1(kf) : kf;
+                    sum = e < D * M ? fmaf(ph, la_elt(v, (size_t)(r0 + j) * M + m), sum) : sum + ph;
+                }
+                acc += sum;
+            }
+        }
+        pre[i] = acc;
+    }
+}
+
 // PHASE kAggregates: the chunk aggregates into a.agg (first of three launches).  PHASE
 // kOutputs: the outputs from the chunk's entering state, read from a.agg after la_scan_kernel
 // turned the aggregates into exclusive prefix sums (third launch).  PHASE kOnePass: both, with
@@ -240,11 +296,12 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
     // one pass: chunk-major tickets, so the chunks a chunk waits on hold smaller tickets and
     // are running; otherwise the block index
     int tile = blockIdx.x;
+    bool forced = false;
     if constexpr (PHASE == kOnePass) {
         if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&a.ctrl[kCtrlTicket], 1u);
         __syncthreads();
-        tile = __builtin_amdgcn_readfirstlane(sh.ticket);
-        if (ticket_out_of_range((uint32_t)tile, (uint32_t)a.BH * (uint32_t)a.n_chunks, a.ctrl)) return;
+        tile = (int)remap_ticket((uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket),
+                                 (uint32_t)a.BH * (uint32_t)a.n_chunks, a.ctrl, forced);
     }
     const int bh = PHASE == kOnePass ? tile % a.BH : tile / a.n_chunks;
     const int ci = PHASE == kOnePass ? tile / a.BH : tile % a.n_chunks;
@@ -402,19 +459,24 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         recs.tag_incl = (epoch << 2) | kKindIncl;
         recs.give_up_word = epoch | kCtrlGiveUpMark;
         const bool has_next = ci + 1 < a.n_chunks;
+        forced = forced || launch_forced(a.ctrl);
         if (ci > 0) {
-            if (has_next) {
+            bool have = false;
+            if (!forced) {
+                if (has_next) {
 #pragma unroll
-                for (int i = 0; i < EPT; ++i) {
-                    const int e = threadIdx.x + i * 64 * NW;
-                    if (e < REC) st_word(recs.word(ci, 0, e), chunk_agg(e), recs.tag_agg);
+                    for (int i = 0; i < EPT; ++i) {
+                        const int e = threadIdx.x + i * 64 * NW;
+                        if (e < REC) st_word(recs.word(ci, 0, e), chunk_agg(e), recs.tag_agg);
+                    }
+                    if (threadIdx.x == 0)
+                        __hip_atomic_store(&recs.status[ci], recs.tag_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(&recs.status[ci], recs.tag_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                have = la_look_back<NW, EPT>(a, recs, ci, sh.start, wid, lane, pre);
+            } else {
+                raise_give_up(a.ctrl, recs.give_up_word, lane);
             }
-            if (!la_look_back<NW, EPT>(a, recs, ci, sh.start, wid, lane, pre))
-#pragma unroll
-                for (int i = 0; i < EPT; ++i) pre[i] = 0.f;
+            if (!have) la_rebuild<IO, D, M, NW, EPT>(a, recs, bh, ci, CH, pre);
         }
         if (has_next) {
 #pragma unroll

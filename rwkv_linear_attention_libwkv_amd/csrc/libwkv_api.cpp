@@ -326,6 +326,14 @@ wkv_status wkv_forward_workspace_query(const void* ws, size_t ws_bytes, uint32_t
     return WKV_OK;
 }
 
+wkv_status wkv_workspace_force_give_up(void* ws, size_t ws_bytes, uint32_t launches, hipStream_t stream) {
+    if (!ws) return WKV_EINVAL;
+    const uintptr_t base = align_up(reinterpret_cast<uintptr_t>(ws), kAlign);
+    if (ws_bytes < (base - reinterpret_cast<uintptr_t>(ws)) + (size_t)wkv::kCtrlWords * 4) return WKV_EWORKSPACE;
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(base);
+    return wkv::launch_set_word(ctrl + wkv::kCtrlForce, launches, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+}
+
 wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const float* w, const float* u,
                        const void* k, const void* v, void* y, void* ws, size_t ws_bytes,
                        hipStream_t stream) {

@@ -296,8 +296,10 @@ struct BwdChunk {
 // Exact path for one wave (any input): per token, the forward state is recomputed from
 // the state entering the wave by walking the earlier tokens of the wave again (O(L^2),
 // read from memory, no per-token arrays), and the reverse sums carry their own float64
-// exponent.  Produces the wave's reverse aggregate (pass 0) or its gradients (pass 1).
-template <typename IO, bool OUT, bool GATE>
+// exponent.  Produces the wave's reverse aggregate (pass 0) or its gradients (pass 1);
+// with the gate, pass 0 also writes dL/dr unless WRITE_GR is off (a tile rebuilding
+// another tile's carry writes nothing of that tile).
+template <typename IO, bool OUT, bool GATE, bool WRITE_GR = true>
 __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, const Rev& rin, const WaveRows& w,
                                           Rsrc gyr, Rsrc gkr, Rsrc gvr, Rsrc grr, int nv, bool valid, float& gw,
                                           float& gu) {
@@ -332,7 +334,7 @@ __device__ __forceinline__ Rev exact_wave(const Chan& ch, const Carry& fin, cons
         const float inv = rcp(fmaf(e1, st.b, e2));
         const float yj = fmaf(e1, st.a, e2 * vj) * inv;
         const float qm = gj * inv;
-        if constexpr (GATE && !OUT)  // dL/dr, once (in the aggregate pass)
+        if constexpr (GATE && !OUT && WRITE_GR)  // dL/dr, once (in the aggregate pass)
             if (valid) store_elt<IO>(grr, w.lane_off, so, gj * yj * sigmoid_f(-rj));
         const double qe = -qref;
         if (OUT) {
@@ -474,11 +476,94 @@ __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs
     return true;
 }
 
+// The reverse carry entering chunk ci from the right (ci < n_chunks - 1) without waiting on
+// any other tile, for a tile whose look-back gave up or a launch forced onto that path: from
+// the nearest chunk to the right whose inclusive record is complete (else the end of the
+// sequence, where no later output contributes), leftwards through every chunk between, by
+// its aggregate record when that is complete, else by walking the chunk's tokens backwards
+// from memory with the exact per-token path, its forward state taken from the state dumped
+// at the chunk's start.  Every record word used is validated by its own tag; nothing is
+// waited for.  seq_off: byte offset of this group at time step 0; li: this lane's index.
+template <typename IO, int TILE, bool GATE>
+__device__ __forceinline__ Rev rebuild_rev(const BwdArgs& args, const RevRecs& R, const Chan& ch, int ci, int lane,
+                                           size_t seq_off, uint32_t lane_off, bool cvalid, size_t li) {
+    const double w2 = w2_of(ch);
+    int start = args.n_chunks;
+    Rev P = rev_rec_form(empty_rev());
+    for (int nearest = ci + 1; nearest < args.n_chunks && start == args.n_chunks; nearest += 64) {
+        const int pc = nearest + lane;
+        const uint32_t st = pc < args.n_chunks ? ld_status(&R.status[pc]) : 0u;
+        uint64_t cand = __ballot(pc < args.n_chunks && st == R.tag_incl);
+        while (cand) {
+            const int d = __builtin_ctzll(cand);
+            uint64_t wds[5];
+            bool good = true;
+#pragma unroll
+            for (int q = 0; q < 5; ++q) {
+                wds[q] = ld_word(R.word(nearest + d, 1, q, lane));
+                good = good && word_tag(wds[q]) == R.tag_incl;
+            }
+            if (__all(good)) {
+                start = nearest + d;
+                P = Rev{word_val(wds[0]), word_val(wds[1]), word_val(wds[2]), word_val(wds[3]), (double)word_val(wds[4])};
+                break;
+            }
+            cand &= cand - 1ull;
+        }
+    }
+    const uint32_t row_bytes = (uint32_t)((size_t)args.C * sizeof(IO));
+    constexpr int kHalf = TILE / 2;
+    static_assert(kHalf <= 64, "exact walks address at most 64 rows from one resource");
+#pragma unroll 1
+    for (int m = start - 1; m > ci; --m) {
+        const int len = min(TILE, args.T - m * TILE);
+        uint64_t t[5];
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+            t[q] = ld_word(R.word(m, 0, q, lane));
+            good = good && word_tag(t[q]) == R.tag_agg;
+        }
+        if (__all(good)) {
+            P = advance_rev(P, Rev{word_val(t[0]), word_val(t[1]), word_val(t[2]), word_val(t[3]), (double)word_val(t[4])},
+                            len, w2);
+            continue;
+        }
+        const size_t ti = (size_t)m * args.n_lanes + li;
+        const Carry fin = normalize(Carry{args.fw_a[ti], args.fw_b[ti], (double)args.fw_p[ti]});
+        Rev c = normalize_rev(P);
+        float gw = 0.f, gu = 0.f;  // not used by the aggregate pass
+        for (int half = len > kHalf ? 1 : 0; half >= 0; --half) {
+            const size_t off = seq_off + ((size_t)m * TILE + (size_t)half * kHalf) * row_bytes;
+            Carry fh = fin;
+            if (half)
+                walk_rows_exact<IO>(ch, fh, static_cast<const char*>(args.k) + seq_off + (size_t)m * TILE * row_bytes,
+                                    static_cast<const char*>(args.v) + seq_off + (size_t)m * TILE * row_bytes, lane_off,
+                                    row_bytes, kHalf, cvalid);
+            WaveRows rows;
+            rows.k = make_rsrc(static_cast<const char*>(args.k) + off);
+            rows.v = make_rsrc(static_cast<const char*>(args.v) + off);
+            rows.y = rows.k;
+            rows.r = GATE ? make_rsrc(static_cast<const char*>(args.r) + off) : rows.k;
+            rows.lane_off = lane_off;
+            rows.row_bytes = row_bytes;
+            rows.pair_off = 0;
+            rows.upper = 0;
+            rows.partner = 0;
+            const Rsrc gyr = make_rsrc(static_cast<const char*>(args.gy) + off);
+            const int nvh = half ? len - kHalf : min(len, kHalf);
+            c = exact_wave<IO, false, GATE, false>(ch, fh, c, rows, gyr, gyr, gyr, gyr, nvh, cvalid, gw, gu);
+        }
+        P = rev_rec_form(normalize_rev(c));
+    }
+    return P;
+}
+
 // One tile of the backward scan (see the plan at the top).  Tiles are numbered in the
 // order workgroups start, from the last chunk of the sequence to the first, so every
 // tile this one waits on has started and publishes its aggregate without waiting.
 template <typename IO, int L, int NW, bool GATE>
-__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
+__global__ __launch_bounds__(64 * NW, 4) void bwd_scan_kernel(BwdArgs args) {
     constexpr int TILE = L * NW;
     static_assert(TILE == kBwdTile, "tiles must line up with the dumped forward tiles");
     const int lane = threadIdx.x & 63;
@@ -488,8 +573,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
 
     if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
-    if (ticket_out_of_range((uint32_t)ticket, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl)) return;
+    bool forced = false;
+    const int ticket = (int)remap_ticket((uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket),
+                                         (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl, forced);
     const int g = ticket % args.n_groups;
     const int ci = args.n_chunks - 1 - ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
@@ -539,6 +625,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
     recs.tag_agg = (epoch << 2) | kKindAgg;
     recs.tag_incl = (epoch << 2) | kKindIncl;
     recs.give_up_word = epoch | kCtrlGiveUpMark;
+    forced = forced || launch_forced(args.ctrl);
 
     const Chan ch = make_chan(args.w[cvalid ? c : 0], args.u[cvalid ? c : 0]);
     const double w2 = w2_of(ch);
@@ -622,15 +709,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdArgs args) {
         const Rev agg_rec = rev_rec_form(run);
         Rev rin = rev_rec_form(empty_rev());
         if (has_next) {
-            bool ready = true;
+            bool ready = !forced;
 #pragma unroll
             for (int q = 0; q < 5; ++q) ready = ready && word_tag(nx[q]) == recs.tag_incl;
+            bool have = false;
             if (__all(ready)) {
                 rin = Rev{word_val(nx[0]), word_val(nx[1]), word_val(nx[2]), word_val(nx[3]), (double)word_val(nx[4])};
-            } else {
+                have = true;
+            } else if (!forced) {
                 publish_rev(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-                if (!rev_look_back<TILE>(args, recs, w2, ci, lane, rin)) rin = rev_rec_form(empty_rev());
+                have = rev_look_back<TILE>(args, recs, w2, ci, lane, rin);
+            } else {
+                raise_give_up(args.ctrl, recs.give_up_word, lane);
             }
+            if (!have)
+                rin = rebuild_rev<IO, TILE, GATE>(args, recs, ch, ci, lane, ((size_t)bi * T * C + c_grp) * sizeof(IO),
+                                                  rows.lane_off, cvalid, li);
         }
         if (ci > 0) publish_rev(recs, ci, 1, lane, advance_rev(rin, agg_rec, tile_len, w2), recs.tag_incl);
         rin = normalize_rev(rin);

@@ -17,6 +17,14 @@
 // has already started; every workgroup counts itself done at its end, and the last one
 // resets both counters and advances the epoch for the next launch (every other
 // workgroup has read the epoch and taken its ticket by then).
+//
+// Giving up.  Every wait is bounded.  A tile whose wait gives up does not use a guessed
+// state: it rebuilds the state it needs from what is certain without waiting (the
+// nearest complete inclusive record, the complete aggregate records after it, and, for
+// a tile whose record is missing, that tile's inputs read again from memory), so its
+// results stay correct; the give-up word is raised as a diagnostic, and once it is up
+// every other wait of the launch gives up at its next check.  The host can force this
+// path for a number of launches (kCtrlForce) to test it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,11 +56,19 @@ __device__ __forceinline__ bool raise_give_up(uint32_t* ctrl, uint32_t give_up_w
     return false;
 }
 
-// A wait stops after kMaxSpins polls, or soon after another tile of the launch gave up.
+// A wait stops after kMaxSpins polls, or once another tile of the launch gave up (checked
+// before the first sleep and every 32 polls after it).
 __device__ __forceinline__ bool must_stop(const uint32_t* ctrl, uint32_t give_up_word, uint32_t spin) {
     if (spin >= kMaxSpins) return true;
-    return (spin & 31u) == 31u &&
+    return (spin & 31u) == 0u &&
            __hip_atomic_load(&ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == give_up_word;
+}
+
+// Whether this launch runs every tile on the give-up path from the start (the host asked
+// for it, or the tile's ticket showed the control block was not zero-filled).
+__device__ __forceinline__ bool launch_forced(const uint32_t* ctrl) {
+    return __builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(&ctrl[kCtrlForce], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0u;
 }
 
 constexpr int kWindowWait = -1;      // no usable inclusive record in the window yet
@@ -111,20 +127,22 @@ __device__ __forceinline__ int find_inclusive(const uint32_t* status, int n_chun
     }
 }
 
-// A ticket past the launch's tiles only comes from a workspace that was not zero-filled
-// before its first use, or from two launches sharing one workspace at once: the workgroup
-// does nothing and flags the call.  Such a launch never completes its bookkeeping, so the
-// epoch counter stays where it was; the flag is the mark a completed launch that gave up
-// would have left (its epoch, one behind the counter), which the workspace query reports.
+// A ticket past the launch's tiles only comes from a ticket counter that was not zero
+// before the launch (a workspace never zero-filled, or two launches sharing one at once).
+// The n tickets of the launch are then still n consecutive numbers, so ticket mod n gives
+// every tile to exactly one workgroup; such a workgroup runs its tile on the give-up path
+// (nothing it could wait for is sure to exist) and flags the call with the mark a launch
+// that gave up leaves, one epoch behind the counter, which the workspace query reports.
 // Call with a wave-uniform ticket; every thread of the workgroup gets the same answer.
-__device__ __forceinline__ bool ticket_out_of_range(uint32_t ticket, uint32_t n_tiles, uint32_t* ctrl) {
-    if (ticket < n_tiles) return false;
+__device__ __forceinline__ uint32_t remap_ticket(uint32_t ticket, uint32_t n_tiles, uint32_t* ctrl, bool& forced) {
+    if (ticket < n_tiles) return ticket;
+    forced = true;
     if (threadIdx.x == 0) {
         const uint32_t epoch = __hip_atomic_load(&ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctrl[kCtrlGiveUp], ((epoch - 1u) & kCtrlEpochMask) | kCtrlGiveUpMark, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    return true;
+    return ticket % n_tiles;
 }
 
 // End of a workgroup (one thread): count it done; the last one prepares the next launch.
@@ -133,6 +151,8 @@ __device__ __forceinline__ bool ticket_out_of_range(uint32_t ticket, uint32_t n_
 __device__ __forceinline__ void finish_tile(uint32_t* ctrl, uint32_t n_tiles, uint32_t epoch, bool inherit) {
     const uint32_t done = atomicAdd(&ctrl[kCtrlDone], 1u);
     if (done + 1u != n_tiles) return;
+    const uint32_t force = __hip_atomic_load(&ctrl[kCtrlForce], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (force != 0u) __hip_atomic_store(&ctrl[kCtrlForce], force - 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (inherit) {
         const uint32_t prev = ((epoch - 1u) & kCtrlEpochMask) | kCtrlGiveUpMark;
         if (__hip_atomic_load(&ctrl[kCtrlGiveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == prev)

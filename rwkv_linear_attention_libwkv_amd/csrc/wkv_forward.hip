@@ -473,6 +473,68 @@ __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R
     return true;
 }
 
+// The state entering chunk ci (ci >= 1) without waiting on any other tile, for a tile whose
+// look-back gave up or a launch forced onto that path: from the nearest chunk before ci
+// whose inclusive record is complete (else the start of the sequence: the state in, or the
+// empty state), through every chunk after it, by its aggregate record when that is complete,
+// else by walking the chunk's TILE rows of k and v in memory with the exact per-token
+// recurrence.  Every record word used is validated by its own tag; nothing is waited for, so
+// the result is the state the WKV equation defines whatever the other tiles are doing.
+// rows_k, rows_v: this lane's group at time step 0 of its sequence (channel c_grp).
+template <typename IO, int TILE>
+__device__ __forceinline__ Carry rebuild_prefix(const FwdArgs& args, const TileRecs& R, const Chan& ch, int ci, int lane,
+                                             const char* rows_k, const char* rows_v, uint32_t lane_off, bool cvalid,
+                                             size_t si) {
+    // nearest complete inclusive record, 64 chunks per look, nothing waited for
+    int start = -1;
+    Carry P{0.f, 0.f, 0.0};
+    for (int nearest = ci - 1; nearest >= 0 && start < 0; nearest -= 64) {
+        const int pc = nearest - lane;
+        const uint32_t st = pc >= 0 ? ld_status(&R.status[pc]) : 0u;
+        uint64_t cand = __ballot(pc >= 0 && st == R.tag_incl);
+        while (cand) {
+            const int d = __builtin_ctzll(cand);
+            uint64_t wds[3];
+            bool good = true;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                wds[q] = ld_word(R.word(nearest - d, 1, q, lane));
+                good = good && word_tag(wds[q]) == R.tag_incl;
+            }
+            if (__all(good)) {
+                start = nearest - d;
+                P = Carry{word_val(wds[0]), word_val(wds[1]), (double)word_val(wds[2])};
+                break;
+            }
+            cand &= cand - 1ull;
+        }
+    }
+    if (start < 0)
+        P = rec_form((args.sin_a && cvalid) ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
+                                             : empty_carry());
+    const double decay = (double)TILE * w2_of(ch);
+    const uint32_t row_bytes = (uint32_t)((size_t)args.C * sizeof(IO));
+#pragma unroll 1
+    for (int m = start + 1; m < ci; ++m) {
+        uint64_t t[3];
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            t[q] = ld_word(R.word(m, 0, q, lane));
+            good = good && word_tag(t[q]) == R.tag_agg;
+        }
+        if (__all(good)) {
+            P = advance(P, Carry{word_val(t[0]), word_val(t[1]), (double)word_val(t[2])}, decay);
+        } else {
+            Carry cw = normalize(P);
+            const size_t off = (size_t)m * TILE * row_bytes;
+            walk_rows_exact<IO>(ch, cw, rows_k + off, rows_v + off, lane_off, row_bytes, TILE, cvalid);
+            P = rec_form(cw);
+        }
+    }
+    return P;
+}
+
 // Everything a tile's waves share.
 template <int NW, int STASH_ROWS>
 struct TileShared {
@@ -493,7 +555,8 @@ template <typename IO, int L, int NW, bool FAST, bool GATE>
 __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Chunk<IO, L>::kStashRows>& sh,
                                           const TileRecs& recs, const WaveRows& rows, Chunk<IO, L>& chunk,
                                           const Chan& ch, float R, int lane, int wid, int ci, int bi, int c,
-                                          bool cvalid, int nv, int t_tile, int tile_len, int g) {
+                                          bool cvalid, int nv, int t_tile, int tile_len, int g, bool forced,
+                                          size_t seq_off) {
     constexpr int TILE = L * NW;
     const int C = args.C, T = args.T;
 
@@ -534,26 +597,33 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
         }
         const Carry agg_rec = rec_form(run);
         Carry prefix;
+        const size_t si = (size_t)bi * C + c;
         if (ci == 0) {
-            const size_t si = (size_t)bi * C + c;
             prefix = rec_form((args.sin_a && cvalid) ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
                                                       : empty_carry());
         } else {
-            bool ready = true;
+            bool ready = !forced;
 #pragma unroll
             for (int q = 0; q < 3; ++q) ready = ready && word_tag(pv[q]) == recs.tag_incl;
+            bool have = false;
             if (__all(ready)) {
                 prefix = Carry{word_val(pv[0]), word_val(pv[1]), (double)word_val(pv[2])};
-            } else {
+                have = true;
+            } else if (!forced) {
                 publish(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-                if (!look_back<TILE, fold_batch<IO>()>(args, recs, ch, ci, lane, prefix)) prefix = empty_carry();
+                have = look_back<TILE, fold_batch<IO>()>(args, recs, ch, ci, lane, prefix);
+            } else {
+                raise_give_up(args.ctrl, recs.give_up_word, lane);
+            }
+            if (!have) {
+                prefix = rebuild_prefix<IO, TILE>(args, recs, ch, ci, lane, static_cast<const char*>(args.k) + seq_off,
+                                                  static_cast<const char*>(args.v) + seq_off, rows.lane_off, cvalid, si);
             }
         }
         const Carry incl = advance(prefix, agg_rec, (double)tile_len * w2_of(ch));
         if (ci + 1 < args.n_chunks) {
             publish(recs, ci, 1, lane, incl, recs.tag_incl);
         } else if (args.sout_a && cvalid) {
-            const size_t si = (size_t)bi * C + c;
             carry_to_abi(incl, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
         }
         sh.ca[lane] = prefix.a;
@@ -596,7 +666,7 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
 }
 
 template <typename IO, int L, int NW, bool GATE>
-__global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
+__global__ __launch_bounds__(64 * NW, NW >= 2 ? 4 : 1) void fwd_chunked_kernel(FwdArgs args) {
     constexpr int TILE = L * NW;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
@@ -607,8 +677,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     // has already started and publishes its aggregate without waiting for anything.
     if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
     __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(sh.ticket);
-    if (ticket_out_of_range((uint32_t)ticket, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl)) return;
+    bool forced = false;
+    const int ticket = (int)remap_ticket((uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket),
+                                         (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl, forced);
     const int g = ticket % args.n_groups;
     const int ci = ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
@@ -638,6 +709,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
 
     // read after the loads are issued; constant during the launch
     const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
+    forced = forced || launch_forced(args.ctrl);
     TileRecs recs;
     recs.rec = static_cast<uint64_t*>(args.recs) + (size_t)g * 6 * 64;
     recs.chunk_words = (size_t)args.n_groups * 6 * 64;
@@ -653,16 +725,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_chunked_kernel(FwdArgs args) {
     const float R = kmax * kLog2e;
     // the fast path takes full chunks only; the one ragged chunk at the end of a
     // sequence (and any ill-conditioned chunk) walks its rows exactly
+    const size_t seq_off = ((size_t)bi * T * C + c_grp) * sizeof(IO);  // time step 0 of this group
     if (__all(chunk_fast_ok(ch, kmax, kmin)) && nv == L)
         tile_body<IO, L, NW, true, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
-                                         t_tile, tile_len, g);
+                                         t_tile, tile_len, g, forced, seq_off);
     else
         tile_body<IO, L, NW, false, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
-                                          t_tile, tile_len, g);
+                                          t_tile, tile_len, g, forced, seq_off);
 
     // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
     __syncthreads();
     if (threadIdx.x == 0) finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, false);
+}
+
+// One control word of a workspace set from the stream (no memset: callers may capture it).
+__global__ void set_word_kernel(uint32_t* __restrict__ p, uint32_t value) {
+    if (threadIdx.x == 0) __hip_atomic_store(p, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t s) {
+    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, s, p, value);
+    return hipGetLastError();
 }
 
 // Zero a workspace (the state every workspace must start from).

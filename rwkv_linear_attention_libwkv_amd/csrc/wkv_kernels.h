@@ -12,6 +12,7 @@ namespace wkv {
 // atomics and stalls the reading tile.
 constexpr int kCtrlTicket = 0;   // tile ticket counter (zero between launches)
 constexpr int kCtrlEpoch = 32;   // record epoch: number of completed launches, mod 2^30
+constexpr int kCtrlForce = 40;   // launches still to run as if every wait gave up at once (set by the host)
 constexpr int kCtrlGiveUp = 48;  // (epoch | kCtrlGiveUpMark) once a launch gave up waiting
 constexpr int kCtrlDone = 64;    // workgroups finished in the current launch
 constexpr int kCtrlWords = 128;  // 512 bytes
@@ -58,6 +59,7 @@ hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s);
 // tile: 64, 128, 256 or 512 time steps per workgroup.
 hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s);
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
+hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,
                              float* ob, float* op, long n, hipStream_t s);
 

@@ -148,4 +148,30 @@ __device__ __forceinline__ void lse_walk(const Chan& ch, Carry& c, const WaveRow
     }
 }
 
+// Exact walk over n rows of one lane's channel read from memory (no outputs), advancing c:
+// rows k_base + j * row_bytes (and v alike) at byte offset lane_off, four rows loaded
+// together, the resource rebased every four rows so any n stays within its range.  Lanes
+// with !valid read zeros.  Small on purpose: it runs only on the give-up path, and its
+// registers count against the whole kernel.
+template <typename IO>
+__device__ __forceinline__ void walk_rows_exact(const Chan& ch, Carry& c, const char* k_base, const char* v_base,
+                                                uint32_t lane_off, uint32_t row_bytes, int n, bool valid) {
+    constexpr int kB = 4;
+#pragma unroll 1
+    for (int j0 = 0; j0 < n; j0 += kB) {
+        const Rsrc rk = make_rsrc(k_base + (size_t)j0 * row_bytes);
+        const Rsrc rv = make_rsrc(v_base + (size_t)j0 * row_bytes);
+        float kk[kB], vv[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const bool in = valid && j0 + j < n;
+            kk[j] = in ? load_elt<IO>(rk, lane_off, (uint32_t)j * row_bytes) : 0.f;
+            vv[j] = in ? load_elt<IO>(rv, lane_off, (uint32_t)j * row_bytes) : 0.f;
+        }
+#pragma unroll 1
+        for (int j = 0; j < kB; ++j)
+            if (j0 + j < n) (void)lse_token<false>(ch, c, kk[j], vv[j]);
+    }
+}
+
 }  // namespace wkv

@@ -26,6 +26,7 @@ EXPORTS = (
     "wkv_forward_workspace_bytes",
     "wkv_forward_workspace_init",
     "wkv_forward_workspace_query",
+    "wkv_workspace_force_give_up",
     "wkv_forward",
     "wkv_forward_ex",
     "wkv_forward_state",
@@ -68,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.wkv_forward_workspace_query.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_uint32),
                                                 ctypes.POINTER(ctypes.c_uint32), vp]
     lib.wkv_forward_workspace_query.restype = i32
+    lib.wkv_workspace_force_give_up.argtypes = [vp, sz, ctypes.c_uint32, vp]
+    lib.wkv_workspace_force_give_up.restype = i32
     lib.wkv_forward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wkv_forward.restype = i32
     lib.wkv_forward_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, i32, i64, vp]
@@ -475,8 +478,16 @@ def workspace_query(workspace, stream=None):
     return int(g.value), int(e.value)
 
 
+def force_give_up(workspace, launches: int = 1, stream=None):
+    """Test hook: the next ``launches`` chained-scan launches on ``workspace`` take the give-up
+    path in every tile (entering states rebuilt without waiting); see wkv_workspace_force_give_up."""
+    _check(lib.wkv_workspace_force_give_up(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           int(launches), _stream(stream)), "wkv_workspace_force_give_up")
+
+
 def lookback_error(workspace, stream=None) -> int:
-    """Non-zero if the last chunked call on ``workspace`` gave up waiting in its look-back."""
+    """Non-zero if the last chunked call on ``workspace`` had a tile give up waiting (its outputs
+    are still valid: such tiles rebuild their state without waiting)."""
     return workspace_query(workspace, stream)[0]
 
 

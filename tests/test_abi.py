@@ -120,6 +120,10 @@ def test_workspace_diagnostics_argument_checks():
     # too small for the control block: rejected before any HIP call
     assert wq(P, 255, ctypes.byref(g), ctypes.byref(e), None) == EWS
     assert wq(ctypes.c_void_p(0x1004), 256, ctypes.byref(g), ctypes.byref(e), None) == EWS
+    fg = lib.wkv_workspace_force_give_up
+    assert fg(NULL, 4096, 1, None) == EINVAL
+    assert fg(P, 255, 1, None) == EWS
+    assert fg(ctypes.c_void_p(0x1004), 256, 1, None) == EWS
 
 
 def test_step_argument_checks():
