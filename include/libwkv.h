@@ -152,6 +152,25 @@ wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                        const void* k, const void* v, void* y,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * wkv_forward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument and no allocation of any kind.  The chunked scan's workspace is a
+ * static device array of 32 MiB that the library holds on every GPU it runs
+ * on until the process ends; the first call on a device looks up its address
+ * (hipGetSymbolAddress, with that device current) and clears its launch
+ * counters with a small kernel on `stream`.  Same kernels and results as
+ * wkv_forward.  A problem whose workspace (wkv_forward_workspace_bytes with
+ * WKV_ALGO_AUTO, chunk 0) exceeds 32 MiB gives WKV_EWORKSPACE, before any
+ * launch.  All calls on one GPU share that GPU's array, which keeps the last
+ * call's records: calls that may overlap in time on the same GPU (other
+ * streams, other host threads) race and must not be made.  Other arguments
+ * and errors as wkv_forward.
+ */
+wkv_status wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
+                               const float* w, const float* u,
+                               const void* k, const void* v, void* y, hipStream_t stream);
+
 /* wkv_forward with an explicit algorithm and chunk length (0 = default). */
 wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                           const float* w, const float* u,

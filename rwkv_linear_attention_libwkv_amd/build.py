@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "lib", "libwkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["libwkv_api.cpp", "wkv_forward.hip", "wkv_step.hip", "wkv_backward.hip", "wkv_mix.hip", "la_forward.hip"]
+SOURCES = ["libwkv_api.cpp", "wkv_forward.hip", "wkv_step.hip", "wkv_backward.hip", "wkv_mix.hip", "la_forward.hip",
+           "wkv_noalloc.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

@@ -28,6 +28,7 @@ EXPORTS = (
     "wkv_forward_workspace_query",
     "wkv_workspace_force_give_up",
     "wkv_forward",
+    "wkv_forward_noalloc",
     "wkv_forward_ex",
     "wkv_forward_state",
     "wkv_step",
@@ -73,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.wkv_workspace_force_give_up.restype = i32
     lib.wkv_forward.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wkv_forward.restype = i32
+    lib.wkv_forward_noalloc.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.wkv_forward_noalloc.restype = i32
     lib.wkv_forward_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, i32, i64, vp]
     lib.wkv_forward_ex.restype = i32
     lib.wkv_forward_state.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp,
@@ -241,6 +244,23 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
                                  *(_ptr(t) for t in sin), *(_ptr(t) for t in sout),
                                  ws_ptr, ws_bytes, ALGOS[algo], chunk_len, st), "wkv_forward_state")
     return (y, sout) if return_state else y
+
+
+@_on_stream
+def wkv_forward_noalloc(w, u, k, v, *, y=None, stream=None):
+    """y = WKV(w, u, k, v) through wkv_forward_noalloc: the library's static device array serves
+    as the workspace (nothing allocated by the call; y is allocated here when not given)."""
+    _need(k.dim() == 3 and v.shape == k.shape and k.dtype == v.dtype, "k and v must be [B, T, C] of one dtype")
+    _need(k.is_cuda and k.is_contiguous() and v.is_contiguous(), "k and v must be contiguous GPU tensors")
+    B, T, C = k.shape
+    _need(w.dtype == torch.float32 and u.dtype == torch.float32 and w.numel() == C and u.numel() == C,
+          "w and u must be float32 with C entries")
+    if y is None:
+        y = torch.empty_like(k)
+    _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    _check(lib.wkv_forward_noalloc(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                   _stream(stream)), "wkv_forward_noalloc")
+    return y
 
 
 @_on_stream
