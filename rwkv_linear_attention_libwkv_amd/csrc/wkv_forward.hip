@@ -426,9 +426,35 @@ __device__ __forceinline__ Carry advance(const Carry& prev, const Carry& agg, do
 template <int TILE, int FB>
 __device__ __forceinline__ bool look_back(const FwdArgs& args, const TileRecs& R, const Chan& ch, int ci,
                                           int lane, Carry& out) {
-    const int start = find_inclusive<-1>(R.status, args.n_chunks, ci, lane, R.tag_agg, R.tag_incl, args.ctrl,
-                                         R.give_up_word);
-    if (start < 0) return false;
+    // every poll reads the previous chunk's inclusive record, which ends the search at once when
+    // complete (one round trip instead of the status word's and then the record's), together
+    // with the status words of the 64 chunks before this one
+    int start;
+    for (uint32_t spin = 0;; ++spin) {
+        uint64_t inc[3];
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            inc[q] = ld_word(R.word(ci - 1, 1, q, lane));
+            good = good && word_tag(inc[q]) == R.tag_incl;
+        }
+        const int pc = ci - 1 - lane;
+        const uint32_t st = pc >= 0 ? ld_status(&R.status[pc]) : 0u;
+        if (__all(good)) {
+            out = Carry{word_val(inc[0]), word_val(inc[1]), (double)word_val(inc[2])};
+            return true;
+        }
+        start = scan_window<-1>(st, pc >= 0, ci - 1, ci, R.tag_agg, R.tag_incl);
+        if (start >= 0) break;
+        if (start == kWindowAllReady) {  // 64 aggregates: continue the search beyond the window
+            start = find_inclusive<-1>(R.status, args.n_chunks, ci - 64, lane, R.tag_agg, R.tag_incl, args.ctrl,
+                                       R.give_up_word);
+            if (start < 0) return false;
+            break;
+        }
+        if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
+        __builtin_amdgcn_s_sleep(kPollSleep);
+    }
     // fold forward from the inclusive record of `start` through the aggregates after it,
     // FB aggregates per round; the first round also loads the inclusive record, and a
     // round re-reads its words until every tag matches

@@ -68,6 +68,31 @@ def test_bf16_io():
     check(inp, algos=[("seq", 0), ("chunked", 0), ("chunked", 128), ("chunked", 256), ("chunked", 512)])
 
 
+@pytest.mark.parametrize("k_std", [2.5, 4.0, 6.0])
+def test_bf16_pairs_wide_key_ranges(k_std):
+    """bfloat16 row pairs with wide key spreads: waves whose keys span more than the fast path's
+    range walk their tokens exactly, so these spreads mix both kinds of wave within tiles and
+    along the chain."""
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(B=2, T=3000, C=128, k_std=k_std, seed=31))
+    check(inp, algos=[("chunked", 0), ("chunked", 256)])
+
+
+def test_bf16_pairs_all_negative_keys():
+    """Every key negative (the chunk reference is then the key of smallest magnitude)."""
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(B=1, T=2100, C=128, seed=32))
+    inp["k"] = workloads.round_to_bf16(-np.abs(inp["k"]) - np.float32(0.25))
+    check(inp, algos=[("chunked", 0), ("seq", 0)])
+
+
+def test_bf16_pairs_nan_propagates():
+    inp = workloads.forward_inputs(workloads.FWD_LONG_BF16.with_(B=2, T=1500, C=128, seed=33))
+    inp["k"][0, 600, 3] = np.nan
+    inp["v"][1, 900, 70] = np.nan
+    y = host(run_forward(to_device(inp), "chunked", 0))
+    assert np.all(np.isnan(y[0, 600:, 3])) and np.all(np.isnan(y[1, 900:, 70]))
+    assert np.all(np.isfinite(y[0, :600, 3])) and np.all(np.isfinite(y[:, :, 71:]))
+
+
 def test_bf16_odd_width():
     """bfloat16 with an odd C: no row pairs, one 2-byte channel per lane, at the default tile and
     the longest one, across a ragged last tile."""
