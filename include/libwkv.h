@@ -280,6 +280,28 @@ wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
                            int64_t M, void* out, hipStream_t stream);
 
 /*
+ * Backward of wkv_token_shift (page "Reinventing RNNs for the Transformer Era: RWKV", section
+ * "토큰 변환", the interpolation the time-mixing block trains through): for
+ * L = sum_m sum g_m * out_m,
+ *   gx[b, t, c]   = sum_m mu_m[c] g_m[b, t, c] + (1 - mu_m[c]) g_m[b, t+1, c]   (g at t = T is 0)
+ *   gmu[m, b, c]  = sum_t g_m[b, t, c] (x[b, t, c] - x[b, t-1, c])             (per lane, float32;
+ *                   the [M, C] parameter's gradient is the sum over b)
+ *   gprev[b, c]   = sum_m (1 - mu_m[c]) g_m[b, 0, c]                            (dL/dx_prev)
+ * with x[b, -1, c] = x_prev[b, c] (zero when x_prev is NULL).  x [B, T, C], g [M, B, T, C],
+ * gx [B, T, C] and gprev [B, C] are of dtype dt; mu [M, C] float32; 1 <= M <= 4; gprev may
+ * be NULL (not wanted).  ws: device workspace of at least
+ * wkv_token_shift_backward_workspace_bytes(B, T, C, M) bytes (no initialisation needed): the
+ * per-segment partial sums of gmu, added per lane in a fixed order in float64, so results are
+ * bitwise reproducible.  T = 0 writes zero gmu (and gprev).  Errors as wkv_token_shift, plus
+ * WKV_EWORKSPACE.
+ */
+size_t wkv_token_shift_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M);
+wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const void* x,
+                                    const void* x_prev, const float* mu, int64_t M, const void* g,
+                                    void* gx, float* gmu, void* gprev, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
  * wkv_forward_gated: z = sigmoid(r) * WKV(w, u, k, v) elementwise, the gated
  * value the output projection W_o consumes, with the gate fused into the
  * output stores (one pass; no WKV intermediate in memory).  r and z are

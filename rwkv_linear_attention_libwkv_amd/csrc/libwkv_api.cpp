@@ -442,6 +442,49 @@ wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const 
     return wkv::launch_token_shift(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
 }
 
+size_t wkv_token_shift_backward_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
+    if (!sizes_ok(B, T, C) || M < 1 || M > wkv::kShiftMaxM) return (size_t)-1;
+    if (B == 0 || T == 0 || C == 0) return 0;
+    return (size_t)wkv::token_shift_segments((long)T) * (size_t)M * (size_t)B * (size_t)C * 4 + kAlign;
+}
+
+wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const void* x,
+                                    const void* x_prev, const float* mu, int64_t M, const void* g, void* gx,
+                                    float* gmu, void* gprev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!sizes_ok(B, T, C) || M < 1 || M > wkv::kShiftMaxM) return WKV_EINVAL;
+    if (!dtype_ok(dt)) return WKV_EDTYPE;
+    if (B == 0 || C == 0) return WKV_OK;
+    if (!mu || !gmu) return WKV_EINVAL;
+    if (B * T > INT_MAX || B * T * C > (int64_t)1 << 40) return WKV_EINVAL;
+    if (T == 0) {  // no token: dL/dmu and dL/dx_prev are zero
+        if (wkv::launch_zero_words(gmu, (size_t)(M * B * C), stream) != hipSuccess) return WKV_EHIP;
+        if (!gprev) return WKV_OK;
+        if (dt == WKV_F32) return wkv::launch_zero_words(gprev, (size_t)(B * C), stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+        return wkv::launch_zero_u16(gprev, (long)(B * C), stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+    }
+    if (!x || !g || !gx) return WKV_EINVAL;
+    const size_t need = wkv_token_shift_backward_workspace_bytes(B, T, C, M);
+    if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
+    const size_t vb = 4 * dtype_size(dt);
+    const bool vector = C % 4 == 0 && aligned(x, vb) && aligned(g, vb) && aligned(gx, vb) &&
+                        (!x_prev || aligned(x_prev, vb)) && (!gprev || aligned(gprev, vb));
+    wkv::ShiftBwdArgs a{};
+    a.x = x;
+    a.x_prev = x_prev;
+    a.mu = mu;
+    a.g = g;
+    a.gx = gx;
+    a.gmu = gmu;
+    a.gprev = gprev;
+    a.part = reinterpret_cast<float*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
+    a.B = (int)B;
+    a.T = (int)T;
+    a.C = (int)C;
+    a.M = (int)M;
+    return wkv::launch_token_shift_backward(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK
+                                                                                                : WKV_EHIP;
+}
+
 // Linear-attention workspace: [control words][status word per chunk][records: per chunk, the
 // chunk's aggregate and its inclusive state, D * M + D tagged 64-bit words each] for the one-pass
 // launch, then [per chunk, D * M + D floats] for the three-launch path; a workspace serves both.

@@ -107,6 +107,22 @@ struct ShiftArgs {
 // x_prev, out); otherwise one element per thread.
 hipError_t launch_token_shift(const ShiftArgs& a, int dtype, bool vec, hipStream_t s);
 
+// Backward of the token shift (see wkv_mix.hip).
+struct ShiftBwdArgs {
+    const void* x;       // [B, T, C] dtype
+    const void* x_prev;  // [B, C] dtype or null (zero)
+    const float* mu;     // [M, C]
+    const void* g;       // [M, B, T, C] dtype: dL/dout
+    void* gx;            // [B, T, C] dtype
+    float* gmu;          // [M, B, C] float32, per lane
+    void* gprev;         // [B, C] dtype or null (not wanted)
+    float* part;         // [n_seg][M][B][C] float32 partial sums (workspace)
+    int B, T, C, M;
+};
+hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, bool vec, hipStream_t s);
+long token_shift_segments(long T);
+hipError_t launch_zero_u16(void* p, long n, hipStream_t s);
+
 // Causal linear attention (see la_forward.hip): q, k [BH, N, D], v, out [BH, N, M] of one dtype.
 struct LaArgs {
     const void* q;

@@ -52,6 +52,21 @@ struct Vec<uint16_t, 8> {
         return raw{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
     }
 };
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <>
+struct Vec<uint16_t, 4> {
+    typedef u32x2 raw;
+    static __device__ __forceinline__ void to_f(const raw& r, float (&f)[4]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f[2 * i] = bf_lo(r[i]);
+            f[2 * i + 1] = bf_hi(r[i]);
+        }
+    }
+    static __device__ __forceinline__ raw from_f(const float (&f)[4]) {
+        return raw{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+    }
+};
 template <typename IO>
 struct Vec<IO, 1> {
     typedef IO raw;
@@ -118,6 +133,153 @@ __global__ __launch_bounds__(256) void token_shift_kernel(ShiftArgs a) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) prev[i] = cur[i];
     }
+}
+
+// Backward of the token shift: for L = sum_m sum g_m * out_m,
+//   dL/dx_t      = sum_m mu_m g_{m,t} + (1 - mu_m) g_{m,t+1}    (g_{m,T} = 0)
+//   dL/dmu_m     = sum_t g_{m,t} (x_t - x_{t-1})                 (per (b, c) lane)
+//   dL/dx_prev   = sum_m (1 - mu_m) g_{m,0}.
+// Ownership as in the forward (a vector of 4 channels over kShiftSeg steps); each
+// thread writes dL/dx of its segment and its segment's partial sums of dL/dmu, which
+// token_shift_reduce_kernel adds per lane in segment order in float64 (deterministic, and the
+// sum over T keeps float32 partials of kShiftSeg terms only).
+template <typename IO, int VEC>
+__global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
+    typedef Vec<IO, VEC> V;
+    typedef typename V::raw raw;
+    const long nv = a.C / VEC;
+    const long n_seg = (a.T + kShiftSeg - 1) / kShiftSeg;
+    const long tid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tid >= (long)a.B * n_seg * nv) return;
+    const long cv = tid % nv;
+    const long seg = (tid / nv) % n_seg;
+    const long b = tid / (nv * n_seg);
+    const long c0 = cv * VEC;
+
+    float mu[kShiftMaxM][VEC];
+#pragma unroll
+    for (int m = 0; m < kShiftMaxM; ++m)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) mu[m][i] = m < a.M ? a.mu[(long)m * a.C + c0 + i] : 0.f;
+
+    const raw* x = static_cast<const raw*>(a.x) + (b * a.T) * nv + cv;
+    const raw* g = static_cast<const raw*>(a.g) + (b * a.T) * nv + cv;
+    raw* gx = static_cast<raw*>(a.gx) + (b * a.T) * nv + cv;
+    const long plane = (long)a.B * a.T * nv;  // vectors per mix of g
+    const long t0 = seg * kShiftSeg;
+    const int n = (int)min((long)kShiftSeg, (long)a.T - t0);
+    float prev[VEC];
+    if (t0 > 0) {
+        V::to_f(__builtin_nontemporal_load(x + (t0 - 1) * nv), prev);
+    } else if (a.x_prev) {
+        V::to_f(static_cast<const raw*>(a.x_prev)[b * nv + cv], prev);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) prev[i] = 0.f;
+    }
+    float gmu[kShiftMaxM][VEC];
+    float gcur[kShiftMaxM][VEC];  // g_{m,t}
+#pragma unroll
+    for (int m = 0; m < kShiftMaxM; ++m)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            gmu[m][i] = 0.f;
+            gcur[m][i] = 0.f;
+        }
+#pragma unroll
+    for (int m = 0; m < kShiftMaxM; ++m)
+        if (m < a.M) V::to_f(__builtin_nontemporal_load(g + m * plane + t0 * nv), gcur[m]);
+    if (seg == 0 && a.gprev) {  // dL/dx_prev = sum_m (1 - mu_m) g_{m,0}
+        float gp[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) gp[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < kShiftMaxM; ++m)
+            if (m < a.M)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) gp[i] = fmaf(1.f - mu[m][i], gcur[m][i], gp[i]);
+        static_cast<raw*>(a.gprev)[b * nv + cv] = V::from_f(gp);
+    }
+#pragma unroll 1
+    for (int j = 0; j < n; ++j) {
+        const long t = t0 + j;
+        float cur[VEC], d[VEC], o[VEC];
+        V::to_f(__builtin_nontemporal_load(x + t * nv), cur);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            d[i] = cur[i] - prev[i];
+            o[i] = 0.f;
+            prev[i] = cur[i];
+        }
+        const bool last = t + 1 >= a.T;
+#pragma unroll
+        for (int m = 0; m < kShiftMaxM; ++m) {
+            if (m >= a.M) break;
+            float gn[VEC];
+            if (last) {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) gn[i] = 0.f;
+            } else {
+                V::to_f(__builtin_nontemporal_load(g + m * plane + (t + 1) * nv), gn);
+            }
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                o[i] = fmaf(mu[m][i], gcur[m][i], fmaf(1.f - mu[m][i], gn[i], o[i]));
+                gmu[m][i] = fmaf(gcur[m][i], d[i], gmu[m][i]);
+                gcur[m][i] = gn[i];
+            }
+        }
+        __builtin_nontemporal_store(V::from_f(o), gx + t * nv);
+    }
+    // partial sums: part[seg][m][b][c]
+#pragma unroll
+    for (int m = 0; m < kShiftMaxM; ++m) {
+        if (m >= a.M) break;
+        float* dst = a.part + ((seg * a.M + m) * a.B + b) * (long)a.C + c0;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dst[i] = gmu[m][i];
+    }
+}
+
+// dL/dmu per (m, b, c) lane: the segments' partial sums added in segment order in float64.
+__global__ __launch_bounds__(256) void token_shift_reduce_kernel(ShiftBwdArgs a) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long lanes = (long)a.M * a.B * a.C;
+    if (i >= lanes) return;
+    const long n_seg = (a.T + kShiftSeg - 1) / kShiftSeg;
+    double s = 0.0;
+    for (long seg = 0; seg < n_seg; ++seg) s += (double)a.part[seg * lanes + i];
+    a.gmu[i] = (float)s;
+}
+
+template <typename IO, int VEC>
+static hipError_t launch_shift_bwd_t(const ShiftBwdArgs& a, hipStream_t s) {
+    const long n_seg = (a.T + kShiftSeg - 1) / kShiftSeg;
+    const long threads = (long)a.B * n_seg * (a.C / VEC);
+    hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       a);
+    const long lanes = (long)a.M * a.B * a.C;
+    hipLaunchKernelGGL(token_shift_reduce_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// vec: 4 channels per thread (16-byte float32 or 8-byte bfloat16 vectors; C a multiple of 4,
+// x, x_prev, g, gx, gprev aligned to the vector), else one element per thread.
+hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, bool vec, hipStream_t s) {
+    if (dtype == 0) return vec ? launch_shift_bwd_t<float, 4>(a, s) : launch_shift_bwd_t<float, 1>(a, s);
+    return vec ? launch_shift_bwd_t<uint16_t, 4>(a, s) : launch_shift_bwd_t<uint16_t, 1>(a, s);
+}
+
+long token_shift_segments(long T) { return (T + kShiftSeg - 1) / kShiftSeg; }
+
+__global__ void zero_u16_kernel(uint16_t* __restrict__ p, long n) {
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_u16(void* p, long n, hipStream_t s) {
+    const long blocks = n / 256 + 1 < 4096 ? n / 256 + 1 : 4096;
+    hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint16_t*>(p), n);
+    return hipGetLastError();
 }
 
 template <typename IO, int VEC>

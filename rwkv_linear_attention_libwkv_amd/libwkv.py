@@ -38,6 +38,8 @@ EXPORTS = (
     "wkv_forward_save",
     "wkv_backward_saved",
     "wkv_token_shift",
+    "wkv_token_shift_backward_workspace_bytes",
+    "wkv_token_shift_backward",
     "wkv_forward_gated",
     "wkv_backward_gated",
     "wkv_linear_attention_workspace_bytes",
@@ -95,6 +97,10 @@ def _load() -> ctypes.CDLL:
     lib.wkv_backward_saved.restype = i32
     lib.wkv_token_shift.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, vp, vp]
     lib.wkv_token_shift.restype = i32
+    lib.wkv_token_shift_backward_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.wkv_token_shift_backward_workspace_bytes.restype = sz
+    lib.wkv_token_shift_backward.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.wkv_token_shift_backward.restype = i32
     lib.wkv_forward_gated.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.wkv_forward_gated.restype = i32
     lib.wkv_backward_gated.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
@@ -396,6 +402,35 @@ def wkv_token_shift(x, mu, *, x_prev=None, out=None, stream=None):
 
 
 @_on_stream
+def wkv_token_shift_backward(x, mu, g, *, x_prev=None, want_gprev=True, gx=None, gmu=None, gprev=None,
+                             workspace=None, stream=None):
+    """Gradients of sum(g * wkv_token_shift(x, mu, x_prev)) for g [M, B, T, C]: returns
+    (gx [B, T, C] dtype, gmu [M, B, C] float32 per lane, gprev [B, C] dtype or None)."""
+    _need(x.dim() == 3 and x.is_cuda and x.is_contiguous(), "x must be a contiguous [B, T, C] GPU tensor")
+    B, T, C = x.shape
+    _need(mu.dim() == 2 and mu.shape[1] == C and mu.dtype == torch.float32 and mu.is_contiguous(),
+          "mu must be contiguous float32 [M, C]")
+    M = mu.shape[0]
+    _need(g.shape == (M, B, T, C) and g.dtype == x.dtype and g.is_contiguous(), "g must be [M, B, T, C] of x's dtype")
+    if x_prev is not None:
+        _need(x_prev.shape == (B, C) and x_prev.dtype == x.dtype and x_prev.is_contiguous(), "bad x_prev")
+    gx = torch.empty_like(x) if gx is None else gx
+    gmu = torch.empty((M, B, C), dtype=torch.float32, device=x.device) if gmu is None else gmu
+    if want_gprev and gprev is None:
+        gprev = torch.empty((B, C), dtype=x.dtype, device=x.device)
+    need = lib.wkv_token_shift_backward_workspace_bytes(B, T, C, M)
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for the token shift backward")
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wkv_token_shift_backward(B, T, C, _dtype_code(x.dtype), _ptr(x), _ptr(x_prev), _ptr(mu), M, _ptr(g),
+                                        _ptr(gx), _ptr(gmu), _ptr(gprev), _ptr(workspace), ws_bytes, _stream(stream)),
+           "wkv_token_shift_backward")
+    return gx, gmu, gprev
+
+
+@_on_stream
 def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stream=None):
     """z = sigmoid(r) * WKV(w, u, k, v).  With ``saved`` (a uint8 device tensor of
     wkv_saved_states_bytes bytes) also keeps the states for wkv_backward_gated."""
@@ -522,6 +557,7 @@ step = wkv_step
 backward = wkv_backward
 forward_save = wkv_forward_save
 token_shift = wkv_token_shift
+token_shift_backward = wkv_token_shift_backward
 forward_gated = wkv_forward_gated
 backward_gated = wkv_backward_gated
 workspace_bytes = wkv_forward_workspace_bytes

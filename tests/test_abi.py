@@ -224,6 +224,24 @@ def test_token_shift_and_gate_argument_checks():
     assert bg(2, 300, 64, F32, *ptrs, P, wsb - 1, None) == EWS
 
 
+def test_token_shift_backward_argument_checks():
+    def tsb(B, T, C, dt=F32, M=3, x=P, xp=NULL, mu=P, g=P, gx=P, gmu=P, gp=P, ws=P, wsb=1 << 30):
+        return lib.wkv_token_shift_backward(B, T, C, dt, x, xp, mu, M, g, gx, gmu, gp, ws, wsb, None)
+    assert tsb(-1, 4, 4) == EINVAL
+    assert tsb(1, 4, 4, M=0) == EINVAL
+    assert tsb(1, 4, 4, M=5) == EINVAL
+    assert tsb(1, 4, 4, dt=9) == EDTYPE
+    for kw in ({"x": NULL}, {"g": NULL}, {"gx": NULL}, {"mu": NULL}, {"gmu": NULL}):
+        assert tsb(1, 4, 4, **kw) == EINVAL, kw
+    need = lib.wkv_token_shift_backward_workspace_bytes(2, 100, 64, 3)
+    assert need >= 4 * 3 * 2 * 64 * 4  # four 32-step segments of partial sums per (mix, lane)
+    assert tsb(2, 100, 64, ws=NULL, wsb=0) == EWS
+    assert tsb(2, 100, 64, wsb=need - 1) == EWS
+    assert lib.wkv_token_shift_backward_workspace_bytes(2, 100, 64, 0) == ctypes.c_size_t(-1).value
+    assert lib.wkv_token_shift_backward_workspace_bytes(2, 0, 64, 3) == 0
+    assert tsb(0, 4, 4, x=NULL, g=NULL, gx=NULL, ws=NULL, wsb=0) == OK  # empty: nothing to do
+
+
 def test_linear_attention_argument_checks():
     la = lib.wkv_linear_attention
     q = lib.wkv_linear_attention_workspace_bytes

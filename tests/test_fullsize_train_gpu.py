@@ -5,7 +5,8 @@ Workloads: B=8, T=8192, C=2048 float32 (the 8K-context, 1.5B-width layer) and B=
 C=5120 bf16 (64K tokens at 14B width), seeded NumPy inputs (workloads.backward_inputs, with
 the gate r ~ N(0, 2) and the token-shift mixes mu ~ U(0, 1) from their own seeded streams).
 Calls: wkv_backward (recomputing forward), wkv_forward_save + wkv_backward_saved,
-wkv_forward_gated + wkv_backward_gated, wkv_token_shift with three mixes.  Gates as in the
+wkv_forward_gated + wkv_backward_gated, wkv_token_shift with three mixes and its backward
+(dL/dout ~ N(0, 1) from its own seeded stream).  Gates as in the
 smaller tests: gradients 5e-5 (float32; gw, gu always) and 1e-2 (bf16 gk, gv, gr), the forward's
 2e-5 / 1e-2, the token shift's 1e-6 / 4e-3 of |mu x_t| + |(1 - mu) x_{t-1}|.
 """
@@ -13,8 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import scaled_error, token_shift, wkv_backward_recurrent, wkv_gated_backward_recurrent, \
-    wkv_gated_recurrent
+from oracle import scaled_error, token_shift, token_shift_backward, wkv_backward_recurrent, \
+    wkv_gated_backward_recurrent, wkv_gated_recurrent
 from rwkv_linear_attention_libwkv_amd import libwkv, workloads
 from tests.gpu_util import TOL, TORCH_DT, host
 from tests.test_backward_gpu import TOL_BF16, TOL_F32, grad_error
@@ -70,6 +71,10 @@ def run_training_calls(spec):
     g_gated = [host(x) for x in libwkv.wkv_backward_gated(w, u, k, v, rd, gy, workspace=ws)]
     assert libwkv.lookback_error(ws) == 0
     shift = host(libwkv.wkv_token_shift(k, torch.from_numpy(mu).cuda()))
+    gs = np.random.default_rng(spec.seed + 3_333_333).standard_normal(size=(3, B, T, C), dtype=np.float32)
+    if dt == "bf16":
+        gs = workloads.round_to_bf16(gs)
+    sb = [host(x) for x in libwkv.wkv_token_shift_backward(k, torch.from_numpy(mu).cuda(), to_dev(gs, dt))]
     del k, v, gy, rd, ws, fws
     torch.cuda.empty_cache()
     print(f"  {spec.name}: GPU calls done", flush=True)
@@ -82,7 +87,18 @@ def run_training_calls(spec):
     err = float(np.max(np.abs(shift - ts_ref) / np.maximum(ts_scale, 1e-30)))
     print(f"  {spec.name} token shift x3: {err:.3e}", flush=True)
     assert err <= SHIFT_TOL[dt], err
-    del ts_ref, prev, ts_scale, shift
+    del ts_ref, ts_scale, shift
+    # its backward: dL/dx against the same sums of magnitudes, dL/dmu per lane likewise
+    rx, rmu, rprev = token_shift_backward(inp["k"], mu, gs)
+    g64 = np.abs(gs.astype(np.float64))
+    sx = (np.abs(mu)[:, None, None, :] * g64).sum(axis=0)
+    sx[:, :-1, :] += (np.abs(1.0 - mu)[:, None, None, :] * g64[:, :, 1:, :]).sum(axis=0)
+    err_x = float(np.max(np.abs(sb[0] - rx) / np.maximum(sx, 1e-30)))
+    smu = (g64 * (np.abs(inp["k"])[None] + np.abs(prev)[None])).sum(axis=2)
+    err_mu = float(np.max(np.abs(sb[1] - rmu) / np.maximum(smu, 1e-30)))
+    print(f"  {spec.name} token shift backward: gx {err_x:.3e} gmu {err_mu:.3e}", flush=True)
+    assert err_x <= SHIFT_TOL[dt] and err_mu <= 1e-5, (err_x, err_mu)
+    del rx, rmu, rprev, g64, sx, smu, sb, gs, prev
 
     # plain backward and the saved pair against the reverse recurrence
     ref, scale = wkv_backward_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], inp["gy"], return_scale=True)

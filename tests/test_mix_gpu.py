@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import scaled_error, token_shift, wkv_gated, wkv_gated_backward
+from oracle import scaled_error, token_shift, token_shift_backward, wkv_gated, wkv_gated_backward
 from rwkv_linear_attention_libwkv_amd import libwkv, workloads
 from tests.gpu_util import TORCH_DT, host
 from tests.test_backward_gpu import TOL_BF16, TOL_F32, grad_error
@@ -154,3 +154,56 @@ def test_open_gate_gives_the_plain_backward():
     for name, a, b in zip(("gw", "gu", "gk", "gv"), (gw, gu, gk, gv), ref):
         assert torch.equal(a, b), name
     assert float(gr.abs().max()) < 1e-20
+
+
+# ---- token shift backward ----
+
+SHIFT_BWD_TOL = {"f32": 1e-6, "bf16": 4e-3}
+
+
+def check_shift_backward(B, T, C, M, dtype, prev, seed, want_gprev=True):
+    rng = np.random.default_rng(seed)
+    x = rounded(rng.normal(0, 1, (B, T, C)), dtype)
+    xp = rounded(rng.normal(0, 1, (B, C)), dtype) if prev else None
+    mu = rng.uniform(-0.25, 1.25, (M, C)).astype(np.float32)
+    g = rounded(rng.normal(0, 1, (M, B, T, C)), dtype)
+    gx, gmu, gprev = libwkv.wkv_token_shift_backward(dev(x, dtype), torch.from_numpy(mu).cuda(), dev(g, dtype),
+                                                     x_prev=None if xp is None else dev(xp, dtype),
+                                                     want_gprev=want_gprev)
+    rx, rmu, rprev = token_shift_backward(x, mu, g, x_prev=xp)
+    # scales: the same sums with every term's magnitude
+    g64 = np.asarray(g, dtype=np.float64)
+    am, a1m = np.abs(mu)[:, None, None, :], np.abs(1.0 - mu)[:, None, None, :]
+    sx = (am * np.abs(g64)).sum(axis=0)
+    sx[:, :-1, :] += (a1m * np.abs(g64[:, :, 1:, :])).sum(axis=0)
+    prev64 = np.zeros((B, 1, C)) if xp is None else np.asarray(xp, dtype=np.float64).reshape(B, 1, C)
+    xs = np.concatenate([prev64, np.asarray(x, dtype=np.float64)[:, :-1, :]], axis=1)
+    smu = (np.abs(g64) * (np.abs(x)[None] + np.abs(xs)[None])).sum(axis=2)
+    sprev = (np.abs(1.0 - mu)[:, None, :] * np.abs(g64[:, :, 0, :])).sum(axis=0)
+    err_x = float(np.max(np.abs(host(gx) - rx) / np.maximum(sx, 1e-30)))
+    err_mu = float(np.max(np.abs(host(gmu) - rmu) / np.maximum(smu, 1e-30)))
+    print(f"  shift bwd B={B} T={T} C={C} M={M} {dtype}: gx {err_x:.2e} gmu {err_mu:.2e}", flush=True)
+    assert err_x <= SHIFT_BWD_TOL[dtype], err_x
+    assert err_mu <= 1e-5, err_mu  # float32 partials of 32 terms, float64 across segments
+    if want_gprev:
+        err_p = float(np.max(np.abs(host(gprev) - rprev) / np.maximum(sprev, 1e-30)))
+        assert err_p <= SHIFT_BWD_TOL[dtype], err_p
+    else:
+        assert gprev is None
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,C,M,prev", [(2, 70, 64, 3, True), (1, 33, 40, 4, False), (3, 5, 7, 1, True),
+                                          (1, 1, 8, 2, True), (2, 100, 24, 3, False), (1, 1000, 130, 3, True)])
+def test_token_shift_backward(dtype, B, T, C, M, prev):
+    check_shift_backward(B, T, C, M, dtype, prev, seed=B * 100 + T + C + M)
+
+
+def test_token_shift_backward_without_gprev_and_empty():
+    check_shift_backward(2, 64, 32, 2, "f32", True, seed=5, want_gprev=False)
+    x = torch.zeros((2, 0, 16), device="cuda")
+    mu = torch.rand((3, 16), device="cuda")
+    g = torch.zeros((3, 2, 0, 16), device="cuda")
+    gx, gmu, gprev = libwkv.wkv_token_shift_backward(x, mu, g)
+    torch.cuda.synchronize()
+    assert gmu.shape == (3, 2, 16) and bool((gmu == 0).all()) and bool((gprev == 0).all())
