@@ -3,16 +3,20 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one wkv_forward over the workload (B=8, T=8192, C=2048 float32 by
-default: the long-context, 1.5B-width forward).  The timed region holds K steps
-with inputs resident in HBM, bracketed by torch.cuda.synchronize().  Prints one
-JSON line: elements/s (B*T*C per second), the HBM roofline of the forward kernel
-(algorithmic bytes: read k, v, write y) measured with HIP events on the launch
-stream, and the float64 CPU oracle timed on the host as a reported baseline.
-The other workloads (169M width, 64K-token bf16, the backward and the fused
-time-mixing parts at the 8K-context and 64K-token shapes, causal linear attention at
-the linear-transformer page's shapes, batched decode step) are timed the same way and
-reported under "other_workloads".
+A step is one wkv_forward over the workload (B=1, T=65536, C=5120 bfloat16 by
+default: 64K tokens at the 14B model's width, the largest workload that fits one
+GPU).  The timed region holds K steps with inputs resident in HBM, bracketed by
+torch.cuda.synchronize().  Prints one JSON line: elements/s (B*T*C per second), the
+HBM roofline of the forward kernel (algorithmic bytes: read k, v, write y) measured
+with HIP events on the launch stream, and the float64 CPU oracle timed on the host
+as a reported baseline.  The other workloads (the 8K-context float32 forward with its
+own roofline, the 169M width, the backward and the fused time-mixing parts at the
+8K-context and 64K-token shapes, causal linear attention at the linear-transformer
+page's shapes, batched decode step) are timed the same way and reported under
+"other_workloads".  Every case first runs its kernel back-to-back for SETTLE_S seconds
+(untimed; the GPU's power management needs about 10 ms under this load to leave its
+start-up transient), then its warmup steps, then its timed steps.  Every forward workload is timed on its seeded NumPy inputs
+(workloads.forward_inputs), the inputs the parity tests check.
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ KERNEL_SOURCES = ("wkv_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h"
                   "libwkv_api.cpp")
 BACKWARD_SOURCES = KERNEL_SOURCES + ("wkv_backward.hip",)
 LA_SOURCES = ("la_forward.hip", "wkv_rows.h", "wkv_chain.h", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
+STEP_SOURCES = ("wkv_step.hip", "wkv_device.h", "wkv_kernels.h", "libwkv_api.cpp")
 
 
 def strip_comments(text: str) -> str:
@@ -85,10 +90,35 @@ def measured_traffic(workload: str, sources=KERNEL_SOURCES):
     return entry.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup):
-    """Run fn warmup times, then time `steps` calls with HIP events; returns (total_s, per_call_s)."""
+SETTLE_S = 0.1  # untimed back-to-back work before every case's warmup steps
+TIMED_LOG = []  # (settle calls, warmup calls, timed calls) of every time_launches, in order
+
+
+def settle(fn, seconds=SETTLE_S, batch=8):
+    """Run fn back-to-back (batches of `batch` launches, synchronized per batch) until `seconds`
+    of wall time have passed; returns the number of launches.  Under a heavy sustained load the
+    MI355X's power management takes about 10 ms to settle: a 64K-token bf16 forward measured
+    4000 launches in a row ran 428 -> 525 -> 458 us over its first 20 launches and 401-403 us
+    (median of every later block of 250) after them.  Timing starts in the settled state."""
     import torch
 
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        n += batch
+        torch.cuda.synchronize()
+    return n
+
+
+def time_launches(fn, steps, warmup):
+    """Settle, run fn warmup times, then time `steps` calls with HIP events; returns
+    (total_s, per_call_s)."""
+    import torch
+
+    TIMED_LOG.append((settle(fn), warmup, steps))
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -144,6 +174,22 @@ def cache_flusher():
     return flush, buf
 
 
+_INPUTS = {}  # seeded inputs drawn once per workload (the CPU baseline and the GPU run share them)
+
+
+def inputs_of(spec):
+    from rwkv_linear_attention_libwkv_amd import workloads
+
+    if spec.name not in _INPUTS:
+        _INPUTS[spec.name] = workloads.forward_inputs(spec)
+    return _INPUTS[spec.name]
+
+
+def roofline_of(achieved_gbps, traffic):
+    return {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBS, "traffic": traffic}
+
+
 def forward_case(spec, steps, warmup, gen="numpy"):
     import numpy as np
     import torch
@@ -152,7 +198,7 @@ def forward_case(spec, steps, warmup, gen="numpy"):
 
     dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
     if gen == "numpy":
-        inp = workloads.forward_inputs(spec)
+        inp = inputs_of(spec)
         w = torch.from_numpy(inp["w"]).cuda()
         u = torch.from_numpy(inp["u"]).cuda()
         k = torch.from_numpy(inp["k"]).cuda().to(dt)
@@ -195,7 +241,10 @@ def forward_case(spec, steps, warmup, gen="numpy"):
         "algorithmic_bytes_per_launch": bytes_per_launch,
         "achieved_GBps": bytes_per_launch / per_call / 1e9,
         "algo": "chunked" if need else "seq",
+        "inputs": "seeded NumPy draws (workloads.forward_inputs)" if gen == "numpy" else "seeded torch draws on the GPU",
     }
+    if spec.elements >= 1e8:  # the long-sequence workloads carry their own roofline
+        out["roofline"] = roofline_of(out["achieved_GBps"], measured_traffic(spec.name))
     if cold is not None:
         out["cold_cache"] = cold
     del k, v, y, ws
@@ -285,6 +334,14 @@ def mix_case(spec, steps, warmup):
     mu = torch.rand((3, spec.C), generator=g, device="cuda")
     out = torch.empty((3,) + shape, dtype=dt, device="cuda")
     _, per_shift = time_launches(lambda: libwkv.wkv_token_shift(k, mu, out=out), steps, warmup)
+    # the token shift's backward (out reused as dL/dout)
+    gx = torch.empty_like(k)
+    gmu = torch.empty((3, spec.B, spec.C), device="cuda")
+    gprev = torch.empty((spec.B, spec.C), dtype=dt, device="cuda")
+    sws = torch.empty(libwkv.lib.wkv_token_shift_backward_workspace_bytes(spec.B, spec.T, spec.C, 3),
+                      dtype=torch.uint8, device="cuda")
+    _, per_shift_bwd = time_launches(lambda: libwkv.wkv_token_shift_backward(k, mu, out, gx=gx, gmu=gmu, gprev=gprev,
+                                                                             workspace=sws), steps, warmup)
     n = spec.elements
     res = {
         "workload": spec.name.replace("wkv_fwd", "wkv_mix"),
@@ -292,8 +349,10 @@ def mix_case(spec, steps, warmup):
         "gated_forward_algorithmic_GBps": 4 * elt * n / per_gated / 1e9,  # read k, v, r; write z
         "token_shift3_s": per_shift,
         "token_shift3_algorithmic_GBps": 4 * elt * n / per_shift / 1e9,  # read x; write three mixes
+        "token_shift3_backward_s": per_shift_bwd,
+        "token_shift3_backward_algorithmic_GBps": 5 * elt * n / per_shift_bwd / 1e9,  # read x, 3 g; write gx
     }
-    del k, v, r, z, ws, out
+    del k, v, r, z, ws, out, gx, gmu, gprev, sws
     torch.cuda.empty_cache()
     return res
 
@@ -373,6 +432,7 @@ def step_case(spec, steps, warmup):
         "algorithmic_bytes_per_launch": bytes_per_step,
         "achieved_GBps": bytes_per_step / (per_call / spec.steps) / 1e9,
     }
+    out["roofline"] = roofline_of(out["achieved_GBps"], measured_traffic(spec.name, STEP_SOURCES))
     del kv, a, b, p, y
     torch.cuda.empty_cache()
     return out
@@ -393,6 +453,16 @@ def _oracle_slice(sl):
 
 
 def _cpu_model():
+    """lscpu's model name (falls back to /proc/cpuinfo)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
@@ -404,8 +474,9 @@ def _cpu_model():
 
 def cpu_baseline(spec, budget_s=20.0, max_workers=16):
     """The float64 oracle (wkv_recurrent) on a bounded sample of the workload, on the host:
-    one process, then the same sample split by channels over the cores this process may use
-    (at most max_workers forked processes).  Must run before anything touches the GPU (the
+    one process, then the same sample split by channels over the cores this process may use,
+    at most max_workers forked processes (16: the host share of one GPU on the boxes this
+    runs on, whatever the affinity mask shows).  Must run before anything touches the GPU (the
     workers are forked)."""
     import multiprocessing
 
@@ -415,7 +486,7 @@ def cpu_baseline(spec, budget_s=20.0, max_workers=16):
     from rwkv_linear_attention_libwkv_amd import workloads
 
     global _CPU_INPUTS
-    inp = workloads.forward_inputs(spec)
+    inp = inputs_of(spec)
     # probe the cost per token, then size the sample (all lanes, leading tokens) to the budget
     t0 = time.perf_counter()
     wkv_recurrent(inp["w"], inp["u"], inp["k"][:, :64], inp["v"][:, :64])
@@ -427,7 +498,8 @@ def cpu_baseline(spec, budget_s=20.0, max_workers=16):
     elements = spec.B * n_tok * spec.C
     single = {"value": elements / dt, "unit": "elements/s", "cores": 1, "seconds": dt}
 
-    n = max(1, min(max_workers, len(os.sched_getaffinity(0)), spec.C))
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(max_workers, affinity, spec.C))
     bounds = np.linspace(0, spec.C, n + 1).astype(int)
     slices = [(int(bounds[i]), int(bounds[i + 1]), n_tok) for i in range(n)]
     _CPU_INPUTS = (inp["w"], inp["u"], inp["k"], inp["v"])
@@ -457,6 +529,8 @@ def cpu_baseline(spec, budget_s=20.0, max_workers=16):
         "single_process": single,
         "direct_definition": direct,
         "cpu_model": _cpu_model(),
+        "affinity_cores": affinity,
+        "worker_cap": max_workers,
         "numpy": np.__version__,
     }
 
@@ -472,18 +546,26 @@ def profile_run(name, launches):
 
     if name in workloads.FORWARD_SPECS:
         spec = workloads.FORWARD_SPECS[name]
-        r = forward_case(spec, launches, 1, gen="torch")
+        r = forward_case(spec, launches, 1)
         print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch", flush=True)
+        per_call, before = 1, 0
     elif name in workloads.LA_SPECS:
         r = la_case(workloads.LA_SPECS[name], launches, 1)
         print(f"# {name}: {r['per_call_s'] * 1e6:.1f} us/call", flush=True)
+        per_call, before = 1, 0
     elif name.replace("wkv_bwd", "wkv_fwd") in workloads.FORWARD_SPECS:
         spec = workloads.FORWARD_SPECS[name.replace("wkv_bwd", "wkv_fwd")]
         r = backward_case(spec, launches, 1)
         print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/call", flush=True)
+        per_call, before = 1, 0
     else:
         r = step_case(workloads.STEP_DECODE, 4, 1)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step", flush=True)
+        per_call, before = workloads.STEP_DECODE.steps, workloads.STEP_DECODE.prefix
+    # the case's first timed block, in launches of its main kernel (one per call; the decode
+    # step: `steps` per call, after the untimed prefix)
+    n_settle, n_warm, n_timed = TIMED_LOG[0]
+    print(f"# timed block: skip {before + per_call * (n_settle + n_warm)} take {per_call * n_timed}", flush=True)
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -497,7 +579,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wkv_fwd_f32_B8_T8192_C2048")
+    ap.add_argument("--workload", default="wkv_fwd_bf16_B1_T65536_C5120")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="time only the main workload")
     ap.add_argument("--profile-run", action="store_true",
@@ -526,9 +608,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile_run:
-        profile_run(args.workload, max(1, min(args.steps, 5)))
+        profile_run(args.workload, max(1, min(args.steps, 20)))
         return
     main_res = forward_case(spec, args.steps, args.warmup)
+    _INPUTS.pop(spec.name, None)
     print(f"# {spec.name}: {main_res['per_launch_s'] * 1e6:.1f} us/launch, "
           f"{main_res['achieved_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -537,8 +620,8 @@ def main():
         for name, s in workloads.FORWARD_SPECS.items():
             if name == spec.name or s.elements < 1e6:
                 continue
-            gen = "torch" if s.elements > 2e8 else "numpy"
-            r = forward_case(s, max(5, args.steps // 2), 2, gen=gen)
+            r = forward_case(s, max(5, args.steps // 2), 2)
+            _INPUTS.pop(s.name, None)
             others.append(r)
             print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/launch, {r['achieved_GBps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
@@ -553,7 +636,9 @@ def main():
             others.append(r)
             print(f"# {r['workload']}: gated forward {r['gated_forward_s'] * 1e6:.1f} us "
                   f"({r['gated_forward_algorithmic_GBps']:.0f} GB/s), token shift x3 {r['token_shift3_s'] * 1e6:.1f} us "
-                  f"({r['token_shift3_algorithmic_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
+                  f"({r['token_shift3_algorithmic_GBps']:.0f} GB/s), its backward "
+                  f"{r['token_shift3_backward_s'] * 1e6:.1f} us ({r['token_shift3_backward_algorithmic_GBps']:.0f} GB/s)",
+                  file=sys.stderr, flush=True)
         for s in workloads.LA_SPECS.values():
             if s.tokens < 100000:
                 continue
@@ -576,6 +661,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": main_res["per_launch_s"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -583,15 +669,8 @@ def main():
         "dtype": "f32" if spec.dtype == "f32" else "bf16",
         "data": "synthetic (seeded NumPy draws; no dataset or weights involved)",
         "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "C": spec.C,
-                   "algo": main_res["algo"], "parallelism": "single GPU"},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-        },
+                   "algo": main_res["algo"], "inputs": main_res["inputs"], "parallelism": "single GPU"},
+        "roofline": roofline_of(achieved, traffic),
         "cpu_baseline": cpu,
         "other_workloads": others,
     }
