@@ -137,8 +137,10 @@ def time_launches(fn, steps, warmup):
 
 def per_launch_stats(fn, n=20, flush=None):
     """Median and min of n single launches, each timed with its own HIP events on the launch
-    stream.  flush: a callable run (and synchronized) before every launch, e.g. a write of a
-    buffer larger than the 256 MB last-level cache so that the launch starts cold."""
+    stream, from an idle GPU.  flush: a callable run before every launch, e.g. a write of a
+    buffer larger than the 256 MB last-level cache so that the launch reads its inputs from HBM;
+    the start event then follows the flush on the stream with no host wait between, so the
+    events bracket the launch itself rather than the idle queue's start-up."""
     import numpy as np
     import torch
 
@@ -148,7 +150,6 @@ def per_launch_stats(fn, n=20, flush=None):
     for _ in range(n):
         if flush is not None:
             flush()
-            torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()

@@ -17,11 +17,15 @@
 // same bits):
 //  * one pass (one launch, q, k, v read once): chunks (workgroups) take tickets in chunk-major
 //    order; a chunk sums its sub-chunk aggregates into the chunk aggregate (phi(K)^T V,
-//    sum phi(K)) and publishes it, finds the state entering it by a decoupled look-back over
-//    the chunks before it in its sequence (the plumbing of the WKV chained scan, wkv_chain.h:
-//    tagged 64-bit record words, status hints, bounded waits), publishes its inclusive state,
-//    and writes its outputs.  Inclusive states follow one chain of float32 additions in chunk
-//    order (a look-back that starts further back repeats the same additions).
+//    sum phi(K)), takes the state entering it from the inclusive state of the chunk before it
+//    in its sequence (the plumbing of the WKV chained scan, wkv_chain.h: tagged 64-bit record
+//    words, status hints, bounded waits), publishes its own inclusive state, and writes its
+//    outputs.  A chunk publishes no aggregate of its own: a state is 1056 words (D = M = 32),
+//    so an aggregate record costs as many bytes as the inclusive one, and measured, a chain of
+//    inclusive states alone was both faster (150.8 against 155.4 us for 64 float32 sequences of
+//    16384, 86.0 against 89.8 us bf16) and moved an eighth fewer bytes than a decoupled
+//    look-back over published aggregates.  Inclusive states follow one chain of float32
+//    additions in chunk order.
 //  * three launches: the chunk aggregates to memory; la_scan_kernel turns them, per sequence
 //    and entry, into exclusive prefix sums in chunk order; the outputs from those.  k and v
 //    are read twice but no chunk waits for another, which wins for few long sequences.
@@ -185,7 +189,8 @@ struct LaRecs {
 // The state entering chunk ci (ci >= 1) for this thread's record entries e = threadIdx.x +
 // i * threads: wave 0 finds the nearest chunk with a published inclusive state and every chunk
 // after it published (find_inclusive); every thread then adds, to that inclusive state, the
-// aggregates of the chunks after it, in chunk order.  False after giving up.
+// aggregates of the chunks after it, in chunk order.  Chunks publish no aggregates, so the
+// search ends at chunk ci - 1 once its inclusive state is out.  False after giving up.
 template <int NW, int EPT>
 __device__ __forceinline__ bool la_look_back(const LaArgs& a, const LaRecs& R, int ci, int& sh_start, int wid,
                                              int lane, float (&pre)[EPT]) {
@@ -463,15 +468,6 @@ __global__ __launch_bounds__(64 * NW) void la_chunk_kernel(LaArgs a) {
         if (ci > 0) {
             bool have = false;
             if (!forced) {
-                if (has_next) {
-#pragma unroll
-                    for (int i = 0; i < EPT; ++i) {
-                        const int e = threadIdx.x + i * 64 * NW;
-                        if (e < REC) st_word(recs.word(ci, 0, e), chunk_agg(e), recs.tag_agg);
-                    }
-                    if (threadIdx.x == 0)
-                        __hip_atomic_store(&recs.status[ci], recs.tag_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
                 have = la_look_back<NW, EPT>(a, recs, ci, sh.start, wid, lane, pre);
             } else {
                 raise_give_up(a.ctrl, recs.give_up_word, lane);
@@ -593,15 +589,15 @@ static hipError_t launch_la_t(const LaArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Positions per chunk: 8 waves of 32 (D = M = 32, float32); 16 waves for D = M = 32 bfloat16,
-// whose chunk work is cheaper, so the chain of look-backs weighs more and halving its length
-// pays for the single workgroup per CU; 8 waves for D = M = 64 (one workgroup per CU either
-// way, its LDS and registers being twice as large).
-int la_chunk_len(int D, int M, int dtype) { return kLaSub * (D * M <= 1024 ? (dtype == 0 ? 8 : 16) : 8); }
+// Positions per chunk: 16 waves of 32 for D = M = 32 (one 1024-thread workgroup per CU: the
+// chain of inclusive states is half as long and its records weigh half as much per byte of
+// q, k, v, out as with 8 waves); 8 waves for D = M = 64 (one workgroup per CU either way, its
+// LDS and registers being twice as large).
+int la_chunk_len(int D, int M, int dtype) { (void)dtype; return kLaSub * (D * M <= 1024 ? 16 : 8); }
 
 hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s) {
     if (a.D == 32 && a.M == 32)
-        return dtype == 0 ? launch_la_t<float, 32, 32, 8>(a, s) : launch_la_t<uint16_t, 32, 32, 16>(a, s);
+        return dtype == 0 ? launch_la_t<float, 32, 32, 16>(a, s) : launch_la_t<uint16_t, 32, 32, 16>(a, s);
     if (a.D == 64 && a.M == 64)
         return dtype == 0 ? launch_la_t<float, 64, 64, 8>(a, s) : launch_la_t<uint16_t, 64, 64, 8>(a, s);
     return hipErrorInvalidValue;

@@ -61,7 +61,7 @@ def test_small(dtype, feature, algo):
 
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 255, 256, 257, 600])
+@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 255, 256, 257, 511, 512, 513, 600, 1100])
 def test_ragged_lengths(dtype, N, algo):
     check(workloads.LA_SMALL.with_(BH=3, N=N, dtype=dtype, seed=N), label="ragged", algo=algo)
 
@@ -121,7 +121,7 @@ def test_deterministic():
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_one_long_sequence(dtype, algo):
-    """BH = 1, N = 16384: 64 chunks chained through one sequence's look-backs, every output
+    """BH = 1, N = 16384: 32 chunks chained through one sequence's look-backs, every output
     against the cumulative-state oracle with its per-element scale."""
     spec = workloads.LA_LONG.with_(BH=1, dtype=dtype, seed=11)
     inp = workloads.linear_attention_inputs(spec)
