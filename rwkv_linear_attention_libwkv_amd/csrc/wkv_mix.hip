@@ -141,9 +141,9 @@ __global__ __launch_bounds__(256) void token_shift_kernel(ShiftArgs a) {
 //   dL/dx_prev   = sum_m (1 - mu_m) g_{m,0}.
 // Ownership as in the forward (a vector of 4 channels over kShiftSeg steps); each
 // thread writes dL/dx of its segment and its segment's partial sums of dL/dmu, which
-// token_shift_reduce_kernel adds per lane in segment order in float64 (deterministic, and the
+// token_shift_reduce_kernel adds per lane in a fixed order in float64 (deterministic, and the
 // sum over T keeps float32 partials of kShiftSeg terms only).
-template <typename IO, int VEC>
+template <typename IO, int VEC, int M>
 __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
     typedef Vec<IO, VEC> V;
     typedef typename V::raw raw;
@@ -156,11 +156,11 @@ __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
     const long b = tid / (nv * n_seg);
     const long c0 = cv * VEC;
 
-    float mu[kShiftMaxM][VEC];
+    float mu[M][VEC];
 #pragma unroll
-    for (int m = 0; m < kShiftMaxM; ++m)
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) mu[m][i] = m < a.M ? a.mu[(long)m * a.C + c0 + i] : 0.f;
+        for (int i = 0; i < VEC; ++i) mu[m][i] = a.mu[(long)m * a.C + c0 + i];
 
     const raw* x = static_cast<const raw*>(a.x) + (b * a.T) * nv + cv;
     const raw* g = static_cast<const raw*>(a.g) + (b * a.T) * nv + cv;
@@ -177,30 +177,31 @@ __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) prev[i] = 0.f;
     }
-    float gmu[kShiftMaxM][VEC];
-    float gcur[kShiftMaxM][VEC];  // g_{m,t}
+    float gmu[M][VEC];
+    float gcur[M][VEC];  // g_{m,t}
 #pragma unroll
-    for (int m = 0; m < kShiftMaxM; ++m)
+    for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
             gmu[m][i] = 0.f;
             gcur[m][i] = 0.f;
         }
 #pragma unroll
-    for (int m = 0; m < kShiftMaxM; ++m)
-        if (m < a.M) V::to_f(__builtin_nontemporal_load(g + m * plane + t0 * nv), gcur[m]);
+    for (int m = 0; m < M; ++m)
+        V::to_f(__builtin_nontemporal_load(g + m * plane + t0 * nv), gcur[m]);
     if (seg == 0 && a.gprev) {  // dL/dx_prev = sum_m (1 - mu_m) g_{m,0}
         float gp[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) gp[i] = 0.f;
 #pragma unroll
-        for (int m = 0; m < kShiftMaxM; ++m)
-            if (m < a.M)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) gp[i] = fmaf(1.f - mu[m][i], gcur[m][i], gp[i]);
+            for (int i = 0; i < VEC; ++i) gp[i] = fmaf(1.f - mu[m][i], gcur[m][i], gp[i]);
         static_cast<raw*>(a.gprev)[b * nv + cv] = V::from_f(gp);
     }
-#pragma unroll 1
+    // two steps per round: the loads of both are in flight together (a bf16 step reads only 8
+    // bytes per lane and array, so one step at a time leaves the loads latency-bound)
+#pragma unroll 2
     for (int j = 0; j < n; ++j) {
         const long t = t0 + j;
         float cur[VEC], d[VEC], o[VEC];
@@ -213,8 +214,7 @@ __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
         }
         const bool last = t + 1 >= a.T;
 #pragma unroll
-        for (int m = 0; m < kShiftMaxM; ++m) {
-            if (m >= a.M) break;
+        for (int m = 0; m < M; ++m) {
             float gn[VEC];
             if (last) {
 #pragma unroll
@@ -233,33 +233,58 @@ __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
     }
     // partial sums: part[seg][m][b][c]
 #pragma unroll
-    for (int m = 0; m < kShiftMaxM; ++m) {
-        if (m >= a.M) break;
+    for (int m = 0; m < M; ++m) {
         float* dst = a.part + ((seg * a.M + m) * a.B + b) * (long)a.C + c0;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) dst[i] = gmu[m][i];
     }
 }
 
-// dL/dmu per (m, b, c) lane: the segments' partial sums added in segment order in float64.
-__global__ __launch_bounds__(256) void token_shift_reduce_kernel(ShiftBwdArgs a) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+// dL/dmu per (m, b, c) lane: the segments' partial sums added in float64, in a fixed order.
+// Block: 64 lanes x kShiftRedSlices slices; slice k adds, in segment order, the k-th of
+// kShiftRedSlices consecutive ranges of segments (loads unrolled by eight, so they are in
+// flight together; a long sequence has thousands of segments per lane), and slice 0 then adds
+// the slices' sums in slice order.
+constexpr int kShiftRedSlices = 8;
+
+__global__ __launch_bounds__(64 * kShiftRedSlices) void token_shift_reduce_kernel(ShiftBwdArgs a) {
+    __shared__ double sums[kShiftRedSlices][64];
+    const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
     const long lanes = (long)a.M * a.B * a.C;
-    if (i >= lanes) return;
+    const long i = (long)blockIdx.x * 64 + lane;
     const long n_seg = (a.T + kShiftSeg - 1) / kShiftSeg;
+    const long per = (n_seg + kShiftRedSlices - 1) / kShiftRedSlices;
+    const long s0 = slice * per, s1 = min(n_seg, s0 + per);
     double s = 0.0;
-    for (long seg = 0; seg < n_seg; ++seg) s += (double)a.part[seg * lanes + i];
-    a.gmu[i] = (float)s;
+    if (i < lanes) {
+#pragma unroll 8
+        for (long seg = s0; seg < s1; ++seg) s += (double)a.part[seg * lanes + i];
+    }
+    sums[slice][lane] = s;
+    __syncthreads();
+    if (slice == 0 && i < lanes) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < kShiftRedSlices; ++k) t += sums[k][lane];
+        a.gmu[i] = (float)t;
+    }
 }
 
 template <typename IO, int VEC>
 static hipError_t launch_shift_bwd_t(const ShiftBwdArgs& a, hipStream_t s) {
     const long n_seg = (a.T + kShiftSeg - 1) / kShiftSeg;
     const long threads = (long)a.B * n_seg * (a.C / VEC);
-    hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       a);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    switch (a.M) {  // the number of mixes sizes the per-thread arrays
+        case 1: hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((token_shift_bwd_kernel<IO, VEC, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     const long lanes = (long)a.M * a.B * a.C;
-    hipLaunchKernelGGL(token_shift_reduce_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(token_shift_reduce_kernel, dim3((unsigned)((lanes + 63) / 64)), dim3(64 * kShiftRedSlices), 0,
+                       s, a);
     return hipGetLastError();
 }
 
