@@ -290,6 +290,11 @@ def backward_case(spec, steps, warmup):
         libwkv.wkv_backward(w, u, k, v, gy, saved=saved, gk=gk, gv=gv, gw=gw, gu=gu, workspace=ws)
 
     _, per_train = time_launches(train, steps, warmup)
+
+    def saved_backward():  # the backward scan (and its small per-lane reduction) alone
+        libwkv.wkv_backward(w, u, k, v, gy, saved=saved, gk=gk, gv=gv, gw=gw, gu=gu, workspace=ws)
+
+    _, per_saved = time_launches(saved_backward, steps, warmup)
     assert libwkv.lookback_error(ws) == 0 and libwkv.lookback_error(fws) == 0, "look-back gave up"
     elt = 4 if spec.dtype == "f32" else 2
     bytes_per_launch = 5 * elt * spec.elements + 8 * spec.B * spec.C  # read k, v, gy; write gk, gv, gw, gu
@@ -304,6 +309,10 @@ def backward_case(spec, steps, warmup):
         "train_pair_s": per_train,
         "train_pair_note": "wkv_forward_save + wkv_backward_saved (y, then all four gradients)",
         "train_pair_algorithmic_GBps": (bytes_per_launch + 3 * elt * spec.elements) / per_train / 1e9,
+        "backward_saved_s": per_saved,
+        "backward_saved_note": "wkv_backward_saved: the backward scan kernel and its per-lane reduction",
+        "roofline": roofline_of(bytes_per_launch / per_saved / 1e9,
+                                measured_traffic(spec.name.replace("wkv_fwd", "wkv_bwd"), BACKWARD_SOURCES)),
     }
     del k, v, gy, gk, gv, ws, y, fws, saved
     torch.cuda.empty_cache()
@@ -545,6 +554,7 @@ def profile_run(name, launches):
 
     from rwkv_linear_attention_libwkv_amd import workloads
 
+    block = 0
     if name in workloads.FORWARD_SPECS:
         spec = workloads.FORWARD_SPECS[name]
         r = forward_case(spec, launches, 1)
@@ -557,15 +567,19 @@ def profile_run(name, launches):
     elif name.replace("wkv_bwd", "wkv_fwd") in workloads.FORWARD_SPECS:
         spec = workloads.FORWARD_SPECS[name.replace("wkv_bwd", "wkv_fwd")]
         r = backward_case(spec, launches, 1)
-        print(f"# {name}: {r['per_launch_s'] * 1e6:.1f} us/call", flush=True)
+        print(f"# {name}: {r['backward_saved_s'] * 1e6:.1f} us/call (wkv_backward_saved)", flush=True)
         per_call, before = 1, 0
+        block = 2  # the saved-states backward: one scan per call, after two blocks of one scan per call
     else:
         r = step_case(workloads.STEP_DECODE, 4, 1)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step", flush=True)
         per_call, before = workloads.STEP_DECODE.steps, workloads.STEP_DECODE.prefix
-    # the case's first timed block, in launches of its main kernel (one per call; the decode
-    # step: `steps` per call, after the untimed prefix)
-    n_settle, n_warm, n_timed = TIMED_LOG[0]
+    # the timed block reported (the case's first, the saved-states backward for a backward
+    # workload), in launches of its main kernel (one per call; the decode step: `steps` per call,
+    # after the untimed prefix)
+    for n_settle, n_warm, n_timed in TIMED_LOG[:block]:
+        before += per_call * (n_settle + n_warm + n_timed)
+    n_settle, n_warm, n_timed = TIMED_LOG[block]
     print(f"# timed block: skip {before + per_call * (n_settle + n_warm)} take {per_call * n_timed}", flush=True)
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").normal_()
     dst = torch.empty_like(src)
@@ -631,7 +645,8 @@ def main():
             others.append(r)
             print(f"# {r['workload']}: {r['per_launch_s'] * 1e6:.1f} us/call, {r['achieved_GBps']:.0f} GB/s "
                   f"(algorithmic bytes); forward_save + backward_saved {r['train_pair_s'] * 1e6:.1f} us, "
-                  f"{r['train_pair_algorithmic_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+                  f"{r['train_pair_algorithmic_GBps']:.0f} GB/s; backward_saved {r['backward_saved_s'] * 1e6:.1f} us, "
+                  f"{r['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
         for s in (workloads.FWD_CTX8K, workloads.FWD_LONG_BF16):
             r = mix_case(s, max(5, args.steps // 2), 2)
             others.append(r)
