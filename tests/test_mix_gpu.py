@@ -194,7 +194,10 @@ def check_shift_backward(B, T, C, M, dtype, prev, seed, want_gprev=True):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,C,M,prev", [(2, 70, 64, 3, True), (1, 33, 40, 4, False), (3, 5, 7, 1, True),
-                                          (1, 1, 8, 2, True), (2, 100, 24, 3, False), (1, 1000, 130, 3, True)])
+                                          (1, 1, 8, 2, True), (2, 100, 24, 3, False), (1, 1000, 130, 3, True),
+                                          # 35, 79 and 129 segments of 32 steps: the dL/dmu reduction's eight
+                                          # slices of segments are ragged, some empty
+                                          (2, 1111, 96, 3, True), (1, 2500, 40, 2, False), (1, 4099, 64, 4, True)])
 def test_token_shift_backward(dtype, B, T, C, M, prev):
     check_shift_backward(B, T, C, M, dtype, prev, seed=B * 100 + T + C + M)
 
