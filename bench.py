@@ -671,7 +671,7 @@ def main():
     achieved = main_res["achieved_GBps"]
     traffic = measured_traffic(spec.name)
     line = {
-        "metric": "WKV fwd elements/sec (B*T*C) and achieved HBM GB/s vs MI355X peak",
+        "metric": "WKV fwd elements/sec (B\u00b7T\u00b7C) and achieved HBM GB/s vs MI355X peak",
         "value": main_res["elements_per_s"],
         "unit": "elements/s",
         "n_gpus": 1,
