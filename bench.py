@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # MI355X dense matrix-core peaks, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources of the forward kernel and its launch path (the committed counter runs are valid
 # for the kernel built from exactly these)
@@ -373,12 +374,12 @@ def la_case(spec, steps, warmup):
 
     from rwkv_linear_attention_libwkv_amd import libwkv
 
+    from rwkv_linear_attention_libwkv_amd import workloads
+
     dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
-    g = torch.Generator(device="cuda")
-    g.manual_seed(spec.seed)
-    q = torch.randn((spec.BH, spec.N, spec.D), generator=g, device="cuda").to(dt)
-    k = torch.randn((spec.BH, spec.N, spec.D), generator=g, device="cuda").to(dt)
-    v = torch.randn((spec.BH, spec.N, spec.M), generator=g, device="cuda").to(dt)
+    inp = workloads.linear_attention_inputs(spec)  # the seeded draws the parity tests use
+    q, k, v = (torch.from_numpy(inp[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    del inp
     out = torch.empty_like(v)
     ws = libwkv.new_la_workspace(spec.BH, spec.N, spec.D, spec.M, dt)
     fn = lambda: libwkv.linear_attention(q, k, v, out=out, workspace=ws)  # noqa: E731
@@ -402,7 +403,13 @@ def la_case(spec, steps, warmup):
         "achieved_GBps": nbytes / per / 1e9,
         "useful_TFLOPs": flops / per / 1e12,
         "traffic_bytes_per_call": measured_traffic(spec.name, LA_SOURCES),
+        "inputs": "seeded NumPy draws (workloads.linear_attention_inputs)",
     }
+    res["roofline"] = roofline_of(res["achieved_GBps"], res["traffic_bytes_per_call"])
+    # the contractions against the dense MFMA peak of their operand type
+    mfma_peak = MFMA_PEAK_TFLOPS["f32" if spec.dtype == "f32" else "bf16"]
+    res["mfma"] = {"achieved": res["useful_TFLOPs"], "peak": mfma_peak, "unit": "TFLOP/s",
+                   "frac": res["useful_TFLOPs"] / mfma_peak}
     if cold is not None:
         res["cold_cache"] = cold
     assert libwkv.lookback_error(ws) == 0, "look-back gave up"

@@ -170,6 +170,26 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _gpu_args(**tensors):
+    """Every given tensor (None entries skipped) is a contiguous tensor on the current GPU.  The
+    kernels take raw device pointers: a host or other-device pointer would fault the GPU, so it
+    is refused here."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _need(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        _need(t.device == dev, f"{name} is on {t.device}, the launch goes to {dev}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _same(name, t, shape, dtype):
+    """A caller's output tensor has the shape and dtype the call writes."""
+    _need(tuple(t.shape) == tuple(shape) and t.dtype == dtype, f"{name} must be {dtype} of shape {tuple(shape)}")
+
+
 def wkv_forward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32, algo: str = "auto",
                                 chunk_len: int = 0) -> int:
     n = lib.wkv_forward_workspace_bytes(B, T, C, _dtype_code(dtype), ALGOS[algo], chunk_len)
@@ -181,6 +201,7 @@ def wkv_forward_workspace_bytes(B: int, T: int, C: int, dtype=torch.float32, alg
 @_on_stream
 def wkv_forward_workspace_init(workspace, stream=None):
     """Zero-fill a forward workspace (needed once, before its first use)."""
+    _gpu_args(workspace=workspace)
     _check(lib.wkv_forward_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                           _stream(stream)), "wkv_forward_workspace_init")
     return workspace
@@ -224,8 +245,7 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
     need = wkv_forward_workspace_bytes(B, T, C, k.dtype, algo, chunk_len)
     if need and workspace is None:
         workspace = new_workspace(B, T, C, k.dtype, algo, chunk_len, device=k.device, stream=stream)
-    if workspace is not None:
-        _need(workspace.is_cuda and workspace.is_contiguous(), "bad workspace")
+    _gpu_args(w=w, u=u, k=k, v=v, y=y, workspace=workspace)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _stream(stream)
@@ -246,6 +266,7 @@ def wkv_forward(w, u, k, v, *, algo: str = "auto", chunk_len: int = 0, y=None, w
         for t in sout:
             _need(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == B * C,
                   "state tensors must be contiguous float32 with B*C entries")
+    _gpu_args(state_a=sin[0], state_b=sin[1], state_p=sin[2], out_a=sout[0], out_b=sout[1], out_p=sout[2])
     _check(lib.wkv_forward_state(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                  *(_ptr(t) for t in sin), *(_ptr(t) for t in sout),
                                  ws_ptr, ws_bytes, ALGOS[algo], chunk_len, st), "wkv_forward_state")
@@ -264,6 +285,7 @@ def wkv_forward_noalloc(w, u, k, v, *, y=None, stream=None):
     if y is None:
         y = torch.empty_like(k)
     _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    _gpu_args(w=w, u=u, k=k, v=v, y=y)
     _check(lib.wkv_forward_noalloc(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                    _stream(stream)), "wkv_forward_noalloc")
     return y
@@ -287,6 +309,7 @@ def wkv_step(w, u, k, v, a, b, p, *, y=None, stream=None):
     if y is None:
         y = torch.empty_like(k)
     _need(y.shape == k.shape and y.dtype == k.dtype and y.is_contiguous(), "bad y")
+    _gpu_args(w=w, u=u, k=k, v=v, a=a, b=b, p=p, y=y)
     _check(lib.wkv_step(N, G, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v),
                         _ptr(a), _ptr(b), _ptr(p), _ptr(y), _stream(stream)), "wkv_step")
     return y
@@ -336,6 +359,7 @@ def wkv_forward_save(w, u, k, v, *, y=None, saved=None, workspace=None, stream=N
     _need(saved.is_cuda and saved.is_contiguous(), "bad saved buffer")
     if workspace is None:
         workspace = new_workspace(B, T, C, k.dtype, "chunked", 0, device=k.device, stream=stream)
+    _gpu_args(w=w, u=u, k=k, v=v, y=y, saved=saved, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.wkv_forward_save(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                 _ptr(saved), saved.numel() * saved.element_size(), _ptr(workspace), ws_bytes,
@@ -370,6 +394,7 @@ def wkv_backward(w, u, k, v, gy, *, saved=None, gk=None, gv=None, gw=None, gu=No
         _need(t.numel() == B * C and t.dtype == torch.float32 and t.is_contiguous(), "bad gw or gu")
     if workspace is None:
         workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device, stream=stream)
+    _gpu_args(w=w, u=u, k=k, v=v, gy=gy, gk=gk, gv=gv, gw=gw, gu=gu, saved=saved, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if saved is None:
         _check(lib.wkv_backward(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
@@ -396,6 +421,7 @@ def wkv_token_shift(x, mu, *, x_prev=None, out=None, stream=None):
         _need(x_prev.shape == (B, C) and x_prev.dtype == x.dtype and x_prev.is_contiguous(), "bad x_prev")
     out = torch.empty((M, B, T, C), dtype=x.dtype, device=x.device) if out is None else out
     _need(out.shape == (M, B, T, C) and out.dtype == x.dtype and out.is_contiguous(), "bad out")
+    _gpu_args(x=x, mu=mu, x_prev=x_prev, out=out)
     _check(lib.wkv_token_shift(B, T, C, _dtype_code(x.dtype), _ptr(x), _ptr(x_prev), _ptr(mu), M, _ptr(out),
                                _stream(stream)), "wkv_token_shift")
     return out
@@ -418,11 +444,16 @@ def wkv_token_shift_backward(x, mu, g, *, x_prev=None, want_gprev=True, gx=None,
     gmu = torch.empty((M, B, C), dtype=torch.float32, device=x.device) if gmu is None else gmu
     if want_gprev and gprev is None:
         gprev = torch.empty((B, C), dtype=x.dtype, device=x.device)
+    _same("gx", gx, (B, T, C), x.dtype)
+    _same("gmu", gmu, (M, B, C), torch.float32)
+    if gprev is not None:
+        _same("gprev", gprev, (B, C), x.dtype)
     need = lib.wkv_token_shift_backward_workspace_bytes(B, T, C, M)
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes for the token shift backward")
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _gpu_args(x=x, mu=mu, g=g, x_prev=x_prev, gx=gx, gmu=gmu, gprev=gprev, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.wkv_token_shift_backward(B, T, C, _dtype_code(x.dtype), _ptr(x), _ptr(x_prev), _ptr(mu), M, _ptr(g),
                                         _ptr(gx), _ptr(gmu), _ptr(gprev), _ptr(workspace), ws_bytes, _stream(stream)),
@@ -445,6 +476,7 @@ def wkv_forward_gated(w, u, k, v, r, *, z=None, saved=None, workspace=None, stre
     algo = "chunked" if saved is not None else "auto"
     if workspace is None:
         workspace = new_workspace(B, T, C, k.dtype, algo, 0, device=k.device, stream=stream)
+    _gpu_args(w=w, u=u, k=k, v=v, r=r, z=z, saved=saved, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb = 0 if saved is None else saved.numel() * saved.element_size()
     _check(lib.wkv_forward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(z),
@@ -459,13 +491,21 @@ def wkv_backward_gated(w, u, k, v, r, gz, *, saved=None, gk=None, gv=None, gr=No
     _need(k.dim() == 3 and all(t.shape == k.shape for t in (v, r, gz)), "k, v, r and gz must be [B, T, C]")
     _need(all(t.dtype == k.dtype and t.is_contiguous() and t.is_cuda for t in (v, r, gz)), "bad v, r or gz")
     B, T, C = k.shape
+    _need(w.dtype == torch.float32 and u.dtype == torch.float32 and w.numel() == C and u.numel() == C,
+          "w and u must be float32 with C entries")
     gk = torch.empty_like(k) if gk is None else gk
     gv = torch.empty_like(k) if gv is None else gv
     gr = torch.empty_like(k) if gr is None else gr
     gw = torch.empty((B, C), dtype=torch.float32, device=k.device) if gw is None else gw
     gu = torch.empty((B, C), dtype=torch.float32, device=k.device) if gu is None else gu
+    for name, t in (("gk", gk), ("gv", gv), ("gr", gr)):
+        _same(name, t, k.shape, k.dtype)
+    for name, t in (("gw", gw), ("gu", gu)):
+        _need(t.numel() == B * C and t.dtype == torch.float32, f"{name} must be float32 with B*C entries")
     if workspace is None:
         workspace = new_backward_workspace(B, T, C, k.dtype, device=k.device, stream=stream)
+    _gpu_args(w=w, u=u, k=k, v=v, r=r, gz=gz, gk=gk, gv=gv, gr=gr, gw=gw, gu=gu, saved=saved,
+              workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb = 0 if saved is None else saved.numel() * saved.element_size()
     _check(lib.wkv_backward_gated(B, T, C, _dtype_code(k.dtype), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
@@ -508,6 +548,7 @@ def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, alg
         raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
     if workspace is None and need:
         workspace = new_la_workspace(BH, N, D, M, q.dtype, device=q.device, stream=stream)
+    _gpu_args(q=q, k=k, v=v, out=out, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.wkv_linear_attention_ex(BH, N, D, M, _dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                        1 if feature_map else 0, _ptr(workspace), ws_bytes, LA_ALGOS[algo],
@@ -526,6 +567,7 @@ def empty_state(shape, device="cuda"):
 
 def workspace_query(workspace, stream=None):
     """(gave_up, epoch) of a forward workspace; synchronises the stream first."""
+    _gpu_args(workspace=workspace)
     g, e = ctypes.c_uint32(0), ctypes.c_uint32(0)
     _check(lib.wkv_forward_workspace_query(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                            ctypes.byref(g), ctypes.byref(e), _stream(stream)),
@@ -536,6 +578,7 @@ def workspace_query(workspace, stream=None):
 def force_give_up(workspace, launches: int = 1, stream=None):
     """Test hook: the next ``launches`` chained-scan launches on ``workspace`` take the give-up
     path in every tile (entering states rebuilt without waiting); see wkv_workspace_force_give_up."""
+    _gpu_args(workspace=workspace)
     _check(lib.wkv_workspace_force_give_up(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                            int(launches), _stream(stream)), "wkv_workspace_force_give_up")
 

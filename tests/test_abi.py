@@ -283,3 +283,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         libwkv._load()
     importlib.reload(libwkv)  # restore the real module state
+
+
+def test_binding_refuses_host_tensors():
+    """Every wrapper refuses host tensors before any GPU call (the C ABI takes raw device pointers
+    and cannot tell them apart); the same checks with one host tensor among GPU ones run in
+    tests/test_binding_gpu.py."""
+    import torch
+
+    B, T, C, M = 2, 8, 4, 3
+    w, u, k, v, gy, r = (torch.ones(C), torch.zeros(C), torch.zeros(B, T, C), torch.zeros(B, T, C),
+                         torch.zeros(B, T, C), torch.zeros(B, T, C))
+    a, b, p = torch.zeros(B, 1, C), torch.zeros(B, 1, C), torch.zeros(B, 1, C)
+    mu, gm = torch.rand(M, C), torch.zeros(M, B, T, C)
+    ws = torch.zeros(1 << 12, dtype=torch.uint8)
+    calls = [
+        lambda: libwkv.wkv_forward(w, u, k, v),
+        lambda: libwkv.wkv_forward_noalloc(w, u, k, v),
+        lambda: libwkv.wkv_step(w.view(1, C), u.view(1, C), k[:, :1].contiguous(), v[:, :1].contiguous(), a, b, p),
+        lambda: libwkv.wkv_forward_save(w, u, k, v),
+        lambda: libwkv.wkv_backward(w, u, k, v, gy),
+        lambda: libwkv.wkv_forward_gated(w, u, k, v, r),
+        lambda: libwkv.wkv_backward_gated(w, u, k, v, r, gy),
+        lambda: libwkv.wkv_token_shift(k, mu),
+        lambda: libwkv.wkv_token_shift_backward(k, mu, gm),
+        lambda: libwkv.linear_attention(torch.zeros(2, 8, 32), torch.zeros(2, 8, 32), torch.zeros(2, 8, 32)),
+        lambda: libwkv.wkv_forward_workspace_init(ws),
+        lambda: libwkv.workspace_query(ws),
+        lambda: libwkv.force_give_up(ws),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError):
+            call()
