@@ -29,6 +29,12 @@
  *    allocate; only wkv_forward_workspace_query synchronises.  The library
  *    keeps no state of its own: what a chunked forward call carries to the
  *    next one (a launch counter) lives in the caller's workspace.
+ *  - Every call except wkv_forward_workspace_query may be captured in a HIP
+ *    graph: workspace counters are set by kernels (no hipMemsetAsync), and
+ *    each chained-scan launch leaves them ready for the next, so a replay
+ *    behaves as the same launch made eagerly.
+ *  - Pointers cannot be checked for being device memory: passing host
+ *    memory faults the GPU.  The Python binding refuses such tensors.
  *  - All argument checks happen before any HIP call.  A negative size, or a
  *    NULL pointer for a non-empty operand, gives WKV_EINVAL; an unknown dtype
  *    gives WKV_EDTYPE; a workspace smaller than the query gives
