@@ -455,6 +455,53 @@ def step_case(spec, steps, warmup):
     return out
 
 
+def decode_graph_case(spec, reps):
+    """Decoding at a small batch, where launches rather than bytes set the pace: the workload's
+    successive steps called one by one from Python, and the same steps captured once in a HIP
+    graph (torch.cuda.CUDAGraph) and replayed, on the same buffers."""
+    import torch
+
+    from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+    w_np, u_np = workloads.step_params(spec)
+    w, u = torch.from_numpy(w_np).cuda(), torch.from_numpy(u_np).cuda()
+    a, b, p = libwkv.empty_state((spec.N, spec.G, spec.C))
+    for s in range(spec.prefix):
+        k, v = workloads.step_kv(spec, s, device="cuda")
+        libwkv.wkv_step(w, u, k, v, a, b, p)
+    kv = [workloads.step_kv(spec, spec.prefix + s, device="cuda") for s in range(spec.steps)]
+    ys = [torch.empty_like(kv[0][0]) for _ in range(spec.steps)]
+
+    def decode():
+        for (k, v), y in zip(kv, ys):
+            libwkv.wkv_step(w, u, k, v, a, b, p, y=y)
+
+    _, per_eager = time_launches(decode, reps, 3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode()
+    _, per_graph = time_launches(graph.replay, reps, 3)
+    bytes_per_step = 30 * spec.lanes
+    out = {
+        "workload": spec.name,
+        "steps_per_decode": spec.steps,
+        "eager_per_step_s": per_eager / spec.steps,
+        "graph_per_step_s": per_graph / spec.steps,
+        "graph_lane_steps_per_s": spec.lanes * spec.steps / per_graph,
+        "graph_achieved_GBps": bytes_per_step / (per_graph / spec.steps) / 1e9,
+        "note": "16 wkv_step calls per decode; eager: one Python call each; graph: one replay of all 16",
+    }
+    del graph, kv, ys, a, b, p
+    torch.cuda.empty_cache()
+    return out
+
+
 _CPU_INPUTS = None  # the oracle sample, inherited by the forked workers of cpu_baseline
 
 
@@ -673,6 +720,10 @@ def main():
         others.append(r)
         print(f"# {r['workload']}: {r['per_step_launch_s'] * 1e6:.1f} us/step, "
               f"{r['achieved_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        r = decode_graph_case(workloads.STEP_DECODE_SMALL, max(10, args.steps))
+        others.append(r)
+        print(f"# {r['workload']}: {r['eager_per_step_s'] * 1e6:.2f} us/step called one by one, "
+              f"{r['graph_per_step_s'] * 1e6:.2f} us/step replayed as one graph", file=sys.stderr, flush=True)
 
     bytes_per_launch = main_res["algorithmic_bytes_per_launch"]
     achieved = main_res["achieved_GBps"]

@@ -89,6 +89,8 @@ FWD_LONG_BF16 = ForwardSpec(
     w_raw_lo=-6.0, w_raw_hi=1.0, u_std=0.5,
 )
 STEP_DECODE = StepSpec("wkv_step_bf16_N256_G32_C4096_x16", 256, 32, 4096, steps=16, prefix=128)
+# one sequence through the same 32 layer slots: launch-bound (4 MB per step)
+STEP_DECODE_SMALL = StepSpec("wkv_step_bf16_N1_G32_C4096_x16", 1, 32, 4096, steps=16, prefix=16)
 
 FORWARD_SPECS = {s.name: s for s in (FWD_SMALL, FWD_169M, FWD_CTX8K, FWD_LONG_BF16)}
 
