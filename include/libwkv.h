@@ -315,10 +315,8 @@ wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, wkv_dtype d
  * the gate (chunked algorithm, the states kept for the backward; workspace of
  * wkv_forward_workspace_bytes(..., WKV_ALGO_CHUNKED, 0)); with `saved` NULL the
  * algorithm is AUTO (workspace of wkv_forward_workspace_bytes(..., WKV_ALGO_AUTO,
- * 0)).  bfloat16 z: the float32 product rounded to nearest even, except with
- * bf16 row pairs in the chunked algorithm (even C, 4-byte aligned arrays),
- * where the gate multiplies the bf16-rounded WKV (within 1.5 units in the last
- * place instead of 0.5).
+ * 0)).  bfloat16 z: the float32 product of the float32 WKV output and the
+ * gate, rounded to nearest even once.
  *
  * wkv_backward_gated: given gz = dL/dz, all of wkv_backward's gradients (for
  * dL/dy = gz * sigmoid(r)) and gr = dL/dr = gz * WKV * sigmoid(r) *

@@ -152,6 +152,7 @@ struct Chunk {
         }
         return Carry{a, b, (double)R};
     }
+    __device__ __forceinline__ void prefetch_gate(const WaveRows&, bool) {}
     // outputs() times sigmoid(r): the gate rows are read into v's registers once v is spent
     __device__ __forceinline__ Carry outputs_gated(const Chan& ch, const Carry& c, float R, const WaveRows& w,
                                                    bool valid) {
@@ -254,27 +255,59 @@ struct Chunk<Bf16Pair, L> {
         }
         return Carry{a, b, (double)R};
     }
-    // outputs() times sigmoid(r): the gate's row-pair words are read into v's registers once v
-    // is spent, then traded with the partner lane.  The packed chunk has no room for float32
-    // outputs, so the gate multiplies the bf16-rounded wkv and the product is rounded again
-    // (within 1.5 bf16 units in the last place of the exact product, against 0.5 elsewhere).
+    // outputs() times sigmoid(r), rounded to bf16 once: the float32 outputs of pair jj stay
+    // unpacked in k[jj] and v[jj] (both spent once the pair is done) until they meet their gate.
+    // The gate's row-pair words of the first kGateAhead pairs are loaded by prefetch_gate()
+    // into registers of their own, before the tile's look-back; once pair jj is gated and
+    // packed, v[jj] is free and takes the gate word of pair jj + kGateAhead.
+    static constexpr int kGateAhead = 16;
+    uint32_t gate_ahead[kGateAhead];
+    __device__ __forceinline__ void prefetch_gate(const WaveRows& w, bool valid) {
+#pragma unroll
+        for (int jj = 0; jj < kGateAhead; ++jj)
+            gate_ahead[jj] = valid ? __builtin_amdgcn_raw_buffer_load_b32(w.r, w.pair_off,
+                                                                          (uint32_t)(2 * jj) * w.row_bytes, kStream)
+                                   : 0u;
+    }
     __device__ __forceinline__ Carry outputs_gated(const Chan& ch, const Carry& c, float R, const WaveRows& w,
                                                    bool valid) {
-        const Carry out = outputs(ch, c, R);
+        fence();
+        const float s = ex2((float)(c.p - (double)R));
+        float a = c.a * s, b = c.b * s;
 #pragma unroll
-        for (int jj = 0; jj < L / 2; ++jj) reg_fence(k[jj]);
+        for (int jj = 0; jj < L / 2; ++jj) {
+            float y[2];
 #pragma unroll
-        for (int jj = 0; jj < L / 2; ++jj)
-            v[jj] = valid ? __builtin_amdgcn_raw_buffer_load_b32(w.r, w.pair_off, (uint32_t)(2 * jj) * w.row_bytes,
-                                                                 kStream)
-                          : 0u;
+            for (int h = 0; h < 2; ++h) {
+                const float kf = h ? bf_hi(k[jj]) : bf_lo(k[jj]);
+                const float vf = h ? bf_hi(v[jj]) : bf_lo(v[jj]);
+                const float x = ex2(fmaf(kf, kLog2e, -R));
+                const float xv = x * vf;
+                y[h] = fmaf(ch.eu, xv, a) * rcp(fmaf(ch.eu, x, b));
+                a = fmaf(ch.d, a, xv);
+                b = fmaf(ch.d, b, x);
+            }
+            k[jj] = __float_as_uint(y[0]);
+            v[jj] = __float_as_uint(y[1]);
+        }
         const uint32_t sel = pair_sel(w.upper);
 #pragma unroll
         for (int jj = 0; jj < L / 2; ++jj) {
-            const uint32_t rw = pair_exchange(v[jj], w.partner, sel);
-            k[jj] = pack_bf16(bf_lo(k[jj]) * sigmoid_f(bf_lo(rw)), bf_hi(k[jj]) * sigmoid_f(bf_hi(rw)));
+            const uint32_t gw = jj < kGateAhead ? gate_ahead[jj] : v[jj - kGateAhead];
+            const uint32_t rw = pair_exchange(gw, w.partner, sel);
+            k[jj] = pack_bf16(__uint_as_float(k[jj]) * sigmoid_f(bf_lo(rw)),
+                              __uint_as_float(v[jj]) * sigmoid_f(bf_hi(rw)));
+            if (jj + kGateAhead < L / 2) {
+                // the load's offset is tied to the packed pair, so the compiler cannot hoist the
+                // load above it (and hold every gate word at once)
+                uint32_t voff = w.pair_off;
+                asm volatile("" : "+v"(voff) : "v"(k[jj]));
+                v[jj] = valid ? __builtin_amdgcn_raw_buffer_load_b32(
+                                    w.r, voff, (uint32_t)(2 * (jj + kGateAhead)) * w.row_bytes, kStream)
+                              : 0u;
+            }
         }
-        return out;
+        return Carry{a, b, (double)R};
     }
     __device__ __forceinline__ void store(const WaveRows& w, bool valid) const { store_pairs<L>(w, valid, k); }
     __device__ __forceinline__ void stash(uint32_t (*st)[64], int lane) const {
@@ -594,6 +627,8 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
         agg = empty_carry();
         lse_walk<IO, false>(ch, agg, rows, nv, cvalid, false);
     }
+    // the gate's first rows load while the tile waits for its entering state
+    if constexpr (FAST && GATE) chunk.prefetch_gate(rows, cvalid);
     sh.a[wid][lane] = agg.a;
     sh.b[wid][lane] = agg.b;
     sh.p[wid][lane] = agg.p;

@@ -95,6 +95,35 @@ def test_gated_forward(dtype, B, T, C, save):
     assert err <= (2e-5 if dtype == "f32" else 1e-2)
 
 
+def test_bf16_gated_is_rounded_float32_gated():
+    """The bf16 gated forward rounds sigma(r) * wkv to bf16 once, from float32 (row pairs too).
+
+    The float32 path on the same bf16-representable inputs gives z32; the bf16 row-pair chunks
+    hold 64 tokens per wave against 32 for float32, which changes the float32 rounding of wkv by
+    up to about 1e-6 of its scale, so every bf16 output must be the rounding of some float32
+    value within 1e-6 * s * sigma(r) of z32 (s: the convex weights applied to |v|), and at
+    least 99% of them the rounding of z32 itself.  A gate applied to the bf16-rounded wkv (two
+    roundings) misses both."""
+    from oracle import wkv_recurrent
+
+    B, T, C = 2, 600, 192
+    inp = gate_inputs(B, T, C, seed=77, dtype="bf16", k_std=1.5)
+    _, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
+    sig = 1.0 / (1.0 + np.exp(-inp["r"].astype(np.float64)))
+    d16 = to_dev(inp)
+    d32 = {n: (t.float() if n in ("k", "v", "r") else t) for n, t in d16.items()}
+    for save in (False, True):
+        saved = torch.empty(libwkv.wkv_saved_states_bytes(B, T, C), dtype=torch.uint8, device="cuda") if save else None
+        z16 = host(libwkv.wkv_forward_gated(d16["w"], d16["u"], d16["k"], d16["v"], d16["r"], saved=saved))
+        saved = torch.empty(libwkv.wkv_saved_states_bytes(B, T, C), dtype=torch.uint8, device="cuda") if save else None
+        z32 = host(libwkv.wkv_forward_gated(d32["w"], d32["u"], d32["k"], d32["v"], d32["r"], saved=saved))
+        d = 1e-6 * s_ref * sig
+        lo = workloads.round_to_bf16((z32 - d).astype(np.float32))
+        hi = workloads.round_to_bf16((z32 + d).astype(np.float32))
+        assert np.all((lo <= z16) & (z16 <= hi)), save
+        assert np.mean(z16 == workloads.round_to_bf16(z32)) >= 0.99, save
+
+
 def test_gated_forward_exact_path():
     """Ill-conditioned waves take the exact per-token path, which applies the gate too."""
     inp = gate_inputs(2, 300, 130, seed=11)
