@@ -347,7 +347,7 @@ wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
  * and q, k used as given (they must then be positive) when it is zero.
  *   q, k : [BH, N, D], v, out : [BH, N, M], dtype dt, dense row-major, each
  *        16-byte aligned (rows move with 16-byte accesses; WKV_EINVAL otherwise).
- * D = M = 32 and D = M = 64 are supported (WKV_EINVAL otherwise).  float32
+ * D and M may each be 32 or 64 (WKV_EINVAL otherwise).  float32
  * inputs use float32 matrix cores; bfloat16 inputs use bf16 matrix cores with
  * float32 accumulation (phi, the masked similarities and the carried state
  * are rounded to bf16 as operands).  Chunks of positions pass their states

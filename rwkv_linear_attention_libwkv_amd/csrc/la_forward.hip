@@ -600,6 +600,10 @@ hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s) {
         return dtype == 0 ? launch_la_t<float, 32, 32, 16>(a, s) : launch_la_t<uint16_t, 32, 32, 16>(a, s);
     if (a.D == 64 && a.M == 64)
         return dtype == 0 ? launch_la_t<float, 64, 64, 8>(a, s) : launch_la_t<uint16_t, 64, 64, 8>(a, s);
+    if (a.D == 32 && a.M == 64)
+        return dtype == 0 ? launch_la_t<float, 32, 64, 8>(a, s) : launch_la_t<uint16_t, 32, 64, 8>(a, s);
+    if (a.D == 64 && a.M == 32)
+        return dtype == 0 ? launch_la_t<float, 64, 32, 8>(a, s) : launch_la_t<uint16_t, 64, 32, 8>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -517,9 +517,12 @@ bool la_one_pass_auto(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt)
     return t_one <= t_three;
 }
 
+// Feature width D and value width M of the kernels built: 32 or 64 each.
+bool la_shape_ok(int64_t D, int64_t M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
+
 size_t wkv_linear_attention_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, wkv_dtype dt) {
     if (BH < 0 || N < 0 || !dtype_ok(dt)) return (size_t)-1;
-    if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return (size_t)-1;
+    if (!la_shape_ok(D, M)) return (size_t)-1;
     if (BH == 0 || N == 0) return 0;
     return la_layout(BH, N, D, M, dt).total;
 }
@@ -529,7 +532,7 @@ wkv_status wkv_linear_attention_ex(int64_t BH, int64_t N, int64_t D, int64_t M, 
                                    size_t ws_bytes, wkv_la_algo algo, hipStream_t stream) {
     if (BH < 0 || N < 0 || BH > INT_MAX || N > INT_MAX) return WKV_EINVAL;
     if (!dtype_ok(dt)) return WKV_EDTYPE;
-    if (!((D == 32 && M == 32) || (D == 64 && M == 64))) return WKV_EINVAL;
+    if (!la_shape_ok(D, M)) return WKV_EINVAL;
     if (algo != WKV_LA_AUTO && algo != WKV_LA_THREE_LAUNCHES && algo != WKV_LA_ONE_PASS) return WKV_EINVAL;
     if (BH == 0 || N == 0) return WKV_OK;
     if (!q || !k || !v || !out) return WKV_EINVAL;

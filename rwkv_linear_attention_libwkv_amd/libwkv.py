@@ -521,7 +521,7 @@ def new_la_workspace(BH: int, N: int, D: int, M: int, dtype=torch.float32, devic
     these sizes (one at a time)."""
     need = lib.wkv_linear_attention_workspace_bytes(BH, N, D, M, _dtype_code(dtype))
     if need == ctypes.c_size_t(-1).value:
-        raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
+        raise ValueError("unsupported linear attention shape (D and M each 32 or 64)")
     if not need:
         return None
     ws = torch.empty((need + 3) // 4 * 4, dtype=torch.uint8, device=device)
@@ -545,7 +545,7 @@ def linear_attention(q, k, v, *, feature_map=True, out=None, workspace=None, alg
     _need(out.shape == v.shape and out.dtype == v.dtype and out.is_contiguous(), "bad out")
     need = lib.wkv_linear_attention_workspace_bytes(BH, N, D, M, _dtype_code(q.dtype))
     if need == ctypes.c_size_t(-1).value:
-        raise ValueError("unsupported linear attention shape (D = M = 32 or 64)")
+        raise ValueError("unsupported linear attention shape (D and M each 32 or 64)")
     if workspace is None and need:
         workspace = new_la_workspace(BH, N, D, M, q.dtype, device=q.device, stream=stream)
     _gpu_args(q=q, k=k, v=v, out=out, workspace=workspace)

@@ -246,7 +246,10 @@ def test_linear_attention_argument_checks():
     la = lib.wkv_linear_attention
     q = lib.wkv_linear_attention_workspace_bytes
     bad = ctypes.c_size_t(-1).value
-    assert q(4, 100, 32, 32, F32) > 0 and q(4, 100, 48, 48, F32) == bad and q(4, 100, 32, 64, F32) == bad
+    assert q(4, 100, 32, 32, F32) > 0 and q(4, 100, 48, 48, F32) == bad and q(4, 100, 16, 16, F32) == bad
+    for D, M in ((32, 64), (64, 32), (64, 64)):  # D and M each 32 or 64
+        assert q(4, 100, D, M, F32) > 0 and q(4, 100, D, M, BF16) > 0
+    assert q(4, 100, 32, 48, F32) == bad and q(4, 100, 128, 64, F32) == bad
     assert q(-1, 100, 32, 32, F32) == bad and q(4, 100, 32, 32, 7) == bad and q(0, 100, 32, 32, F32) == 0
     need = q(4, 100, 32, 32, BF16)
     assert la(4, 100, 48, 48, F32, P, P, P, P, 1, P, need, None) == EINVAL

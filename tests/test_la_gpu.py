@@ -72,6 +72,19 @@ def test_head_dim_64(dtype, algo):
     check(workloads.LA_SMALL.with_(BH=2, N=700, D=64, M=64, dtype=dtype, seed=7), label="D=64", algo=algo)
 
 
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 64), (64, 32)])
+@pytest.mark.parametrize("N", [257, 700])
+def test_feature_and_value_widths_differ(dtype, D, M, N, algo):
+    """q, k of D features and v of M values with D != M (chunks of 256 positions)."""
+    spec = workloads.LA_SMALL.with_(BH=3, N=N, D=D, M=M, dtype=dtype, seed=D + M + N)
+    check(spec, label=f"D={D} M={M}", algo=algo)
+    check(spec, feature=False, label=f"D={D} M={M}", algo=algo)
+    inp = workloads.linear_attention_inputs(spec)
+    assert np.array_equal(run(inp, algo="one"), run(inp, algo="three"))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [32, 64])
 def test_evaluations_agree_bitwise(dtype, D):
