@@ -465,9 +465,14 @@ wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, wkv_dtype d
     if (!x || !g || !gx) return WKV_EINVAL;
     const size_t need = wkv_token_shift_backward_workspace_bytes(B, T, C, M);
     if (!ws || ws_bytes < need) return WKV_EWORKSPACE;
-    const size_t vb = 4 * dtype_size(dt);
-    const bool vector = C % 4 == 0 && aligned(x, vb) && aligned(g, vb) && aligned(gx, vb) &&
-                        (!x_prev || aligned(x_prev, vb)) && (!gprev || aligned(gprev, vb));
+    // channels per thread: 8 (16-byte bf16 vectors, for two or more mixes), 4, or 1, as C and the
+    // alignment of every [*, C] array allow
+    auto fits = [&](int64_t n) {
+        const size_t vb = (size_t)n * dtype_size(dt);
+        return C % n == 0 && aligned(x, vb) && aligned(g, vb) && aligned(gx, vb) && (!x_prev || aligned(x_prev, vb)) &&
+               (!gprev || aligned(gprev, vb));
+    };
+    const int vec = (dt == WKV_BF16 && M >= 2 && fits(8)) ? 8 : fits(4) ? 4 : 1;
     wkv::ShiftBwdArgs a{};
     a.x = x;
     a.x_prev = x_prev;
@@ -481,7 +486,7 @@ wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, wkv_dtype d
     a.T = (int)T;
     a.C = (int)C;
     a.M = (int)M;
-    return wkv::launch_token_shift_backward(a, dt == WKV_F32 ? 0 : 1, vector, stream) == hipSuccess ? WKV_OK
+    return wkv::launch_token_shift_backward(a, dt == WKV_F32 ? 0 : 1, vec, stream) == hipSuccess ? WKV_OK
                                                                                                 : WKV_EHIP;
 }
 

@@ -119,7 +119,7 @@ struct ShiftBwdArgs {
     float* part;         // [n_seg][M][B][C] float32 partial sums (workspace)
     int B, T, C, M;
 };
-hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, bool vec, hipStream_t s);
+hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, int vec, hipStream_t s);
 long token_shift_segments(long T);
 hipError_t launch_zero_u16(void* p, long n, hipStream_t s);
 

@@ -199,9 +199,12 @@ __global__ __launch_bounds__(256) void token_shift_bwd_kernel(ShiftBwdArgs a) {
             for (int i = 0; i < VEC; ++i) gp[i] = fmaf(1.f - mu[m][i], gcur[m][i], gp[i]);
         static_cast<raw*>(a.gprev)[b * nv + cv] = V::from_f(gp);
     }
-    // two steps per round: the loads of both are in flight together (a bf16 step reads only 8
-    // bytes per lane and array, so one step at a time leaves the loads latency-bound)
-#pragma unroll 2
+    // two steps per round, so that the loads of both are in flight together (a bf16 step of 4
+    // channels reads only 8 bytes per lane and array: one step at a time leaves the loads
+    // latency-bound); 8 bf16 channels (16-byte vectors) take one step per round, whose loads
+    // already move as many bytes, since two would cost a wave per SIMD in registers
+    constexpr int kStepsPerRound = (sizeof(IO) == 2 && VEC == 8) ? 1 : 2;
+#pragma unroll kStepsPerRound
     for (int j = 0; j < n; ++j) {
         const long t = t0 + j;
         float cur[VEC], d[VEC], o[VEC];
@@ -288,11 +291,14 @@ static hipError_t launch_shift_bwd_t(const ShiftBwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// vec: 4 channels per thread (16-byte float32 or 8-byte bfloat16 vectors; C a multiple of 4,
-// x, x_prev, g, gx, gprev aligned to the vector), else one element per thread.
-hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, bool vec, hipStream_t s) {
-    if (dtype == 0) return vec ? launch_shift_bwd_t<float, 4>(a, s) : launch_shift_bwd_t<float, 1>(a, s);
-    return vec ? launch_shift_bwd_t<uint16_t, 4>(a, s) : launch_shift_bwd_t<uint16_t, 1>(a, s);
+// vec: channels per thread, 8 (bf16 only: 16-byte vectors), 4 (16-byte float32 or 8-byte bf16
+// vectors) or 1; C a multiple of it and x, x_prev, g, gx, gprev aligned to the vector.  With
+// three bf16 mixes (B=1, T=65536, C=5120), 16-byte vectors: 687.1 against 769.9 us (four mixes
+// 1007.9 against 1179.0); with one mix, 408.4 against 398.7, so one mix keeps 8-byte vectors.
+hipError_t launch_token_shift_backward(const ShiftBwdArgs& a, int dtype, int vec, hipStream_t s) {
+    if (dtype == 0) return vec >= 4 ? launch_shift_bwd_t<float, 4>(a, s) : launch_shift_bwd_t<float, 1>(a, s);
+    if (vec == 8) return launch_shift_bwd_t<uint16_t, 8>(a, s);
+    return vec == 4 ? launch_shift_bwd_t<uint16_t, 4>(a, s) : launch_shift_bwd_t<uint16_t, 1>(a, s);
 }
 
 long token_shift_segments(long T) { return (T + kShiftSeg - 1) / kShiftSeg; }

@@ -226,7 +226,9 @@ def check_shift_backward(B, T, C, M, dtype, prev, seed, want_gprev=True):
                                           (1, 1, 8, 2, True), (2, 100, 24, 3, False), (1, 1000, 130, 3, True),
                                           # 35, 79 and 129 segments of 32 steps: the dL/dmu reduction's eight
                                           # slices of segments are ragged, some empty
-                                          (2, 1111, 96, 3, True), (1, 2500, 40, 2, False), (1, 4099, 64, 4, True)])
+                                          (2, 1111, 96, 3, True), (1, 2500, 40, 2, False), (1, 4099, 64, 4, True),
+                                          # bf16 vectors of 4 channels (C not a multiple of 8; one mix)
+                                          (2, 300, 36, 3, True), (1, 500, 64, 1, False)])
 def test_token_shift_backward(dtype, B, T, C, M, prev):
     check_shift_backward(B, T, C, M, dtype, prev, seed=B * 100 + T + C + M)
 
