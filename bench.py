@@ -363,6 +363,9 @@ def mix_case(spec, steps, warmup):
         "token_shift3_backward_s": per_shift_bwd,
         "token_shift3_backward_algorithmic_GBps": 5 * elt * n / per_shift_bwd / 1e9,  # read x, 3 g; write gx
     }
+    # each call against the HBM peak (algorithmic bytes; no counter run is kept for these)
+    res["rooflines"] = {op: roofline_of(res[op + "_algorithmic_GBps"], None)
+                        for op in ("gated_forward", "token_shift3", "token_shift3_backward")}
     del k, v, r, z, ws, out, gx, gmu, gprev, sws
     torch.cuda.empty_cache()
     return res
