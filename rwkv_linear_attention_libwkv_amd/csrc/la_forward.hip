@@ -590,8 +590,8 @@ static hipError_t launch_la_t(const LaArgs& a, hipStream_t s) {
 
 // Positions per chunk: 16 waves of 32 for D = M = 32 (one 1024-thread workgroup per CU: the
 // chain of inclusive states is half as long and its records weigh half as much per byte of
-// q, k, v, out as with 8 waves); 8 waves for D = M = 64 (one workgroup per CU either way, its
-// LDS and registers being twice as large).
+// q, k, v, out as with 8 waves); 8 waves when D or M is 64 (one workgroup per CU either way for
+// D = M = 64, its LDS and registers being twice as large).
 int la_chunk_len(int D, int M, int dtype) { (void)dtype; return kLaSub * (D * M <= 1024 ? 16 : 8); }
 
 hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s) {

@@ -140,7 +140,7 @@ struct LaArgs {
     int feature;   // apply phi = elu + 1 to q and k
     int one_pass;  // one launch with look-backs, or three launches (aggregates, scan, outputs)
 };
-// Positions per chunk for these head sizes (only D = M = 32 and D = M = 64 are built).
+// Positions per chunk for these head sizes (D and M each 32 or 64 are built).
 int la_chunk_len(int D, int M, int dtype);  // dtype 0 float32, 1 bfloat16
 hipError_t launch_linear_attention(const LaArgs& a, int dtype, hipStream_t s);
 

@@ -139,7 +139,8 @@ __global__ __launch_bounds__(256) void token_shift_kernel(ShiftArgs a) {
 //   dL/dx_t      = sum_m mu_m g_{m,t} + (1 - mu_m) g_{m,t+1}    (g_{m,T} = 0)
 //   dL/dmu_m     = sum_t g_{m,t} (x_t - x_{t-1})                 (per (b, c) lane)
 //   dL/dx_prev   = sum_m (1 - mu_m) g_{m,0}.
-// Ownership as in the forward (a vector of 4 channels over kShiftSeg steps); each
+// A thread owns a vector of channels (4, or 8 bf16 channels, see launch_token_shift_backward)
+// over kShiftSeg steps; each
 // thread writes dL/dx of its segment and its segment's partial sums of dL/dmu, which
 // token_shift_reduce_kernel adds per lane in a fixed order in float64 (deterministic, and the
 // sum over T keeps float32 partials of kShiftSeg terms only).
