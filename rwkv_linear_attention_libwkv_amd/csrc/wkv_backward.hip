@@ -407,9 +407,11 @@ __device__ __forceinline__ void publish_rev(const RevRecs& R, int chunk, int slo
 
 // The carry entering chunk ci from the right (ci < n_chunks - 1): folded from the
 // nearest inclusive record on the right through the aggregates between, in chunk order
-// from right to left, with advance_rev (every chunk between is a full tile).  Each
-// round re-reads its words until every tag matches; gives up like the forward scan.
-template <int TILE>
+// from right to left, with advance_rev (every chunk between is a full tile).  The
+// aggregates are read FB per round, their loads in flight together (one round trip for
+// up to FB tiles of a chain that has fallen behind); each round re-reads its words until
+// every tag matches; gives up like the forward scan.
+template <int TILE, int FB>
 __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs& R, double w2, int ci, int lane,
                                               Rev& out) {
     // every poll reads the inclusive record of chunk ci+1, which ends the search at once when
@@ -440,12 +442,15 @@ __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs
         if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
         __builtin_amdgcn_s_sleep(kPollSleep);
     }
+    // fold from the inclusive record of `start` through the aggregates before it, FB per round
+    // (chunks c0, c0 - 1, ...); the first round also loads the inclusive record, and a round
+    // re-reads its words until every tag matches
     Rev P{0.f, 0.f, 0.f, 0.f, 0.0};
     bool have_p = false;
 #pragma unroll 1
-    for (int c0 = start - 1;; --c0) {
-        uint64_t inc[5], t[5];
-        const bool need_agg = c0 > ci;
+    for (int c0 = start - 1;;) {
+        const int n = min(FB, c0 - ci);
+        uint64_t inc[5], t[FB][5];
         for (uint32_t spin = 0;; ++spin) {
             bool good = true;
             if (!have_p)
@@ -454,12 +459,14 @@ __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs
                     inc[q] = ld_word(R.word(start, 1, q, lane));
                     good = good && word_tag(inc[q]) == R.tag_incl;
                 }
-            if (need_agg)
 #pragma unroll
-                for (int q = 0; q < 5; ++q) {
-                    t[q] = ld_word(R.word(c0, 0, q, lane));
-                    good = good && word_tag(t[q]) == R.tag_agg;
-                }
+            for (int j = 0; j < FB; ++j)
+                if (j < n)
+#pragma unroll
+                    for (int q = 0; q < 5; ++q) {
+                        t[j][q] = ld_word(R.word(c0 - j, 0, q, lane));
+                        good = good && word_tag(t[j][q]) == R.tag_agg;
+                    }
             if (__all(good)) break;
             if (must_stop(args.ctrl, R.give_up_word, spin)) return raise_give_up(args.ctrl, R.give_up_word, lane);
             __builtin_amdgcn_s_sleep(kPollSleep);
@@ -468,9 +475,14 @@ __device__ __forceinline__ bool rev_look_back(const BwdArgs& args, const RevRecs
             P = Rev{word_val(inc[0]), word_val(inc[1]), word_val(inc[2]), word_val(inc[3]), (double)word_val(inc[4])};
             have_p = true;
         }
-        if (!need_agg) break;
-        P = advance_rev(P, Rev{word_val(t[0]), word_val(t[1]), word_val(t[2]), word_val(t[3]), (double)word_val(t[4])},
-                        TILE, w2);
+#pragma unroll
+        for (int j = 0; j < FB; ++j)
+            if (j < n)
+                P = advance_rev(P, Rev{word_val(t[j][0]), word_val(t[j][1]), word_val(t[j][2]), word_val(t[j][3]),
+                                       (double)word_val(t[j][4])},
+                                TILE, w2);
+        c0 -= n;
+        if (c0 <= ci) break;
     }
     out = P;
     return true;
@@ -562,6 +574,11 @@ __device__ __forceinline__ Rev rebuild_rev(const BwdArgs& args, const RevRecs& R
 // One tile of the backward scan (see the plan at the top).  Tiles are numbered in the
 // order workgroups start, from the last chunk of the sequence to the first, so every
 // tile this one waits on has started and publishes its aggregate without waiting.
+// Aggregates folded per look-back round (wave 0's chunk is stashed in LDS by then, so the
+// 40 registers of four records are free; 4 against 1: the same bits, 0.4-0.5% faster for
+// bf16, B=1, T=65536, C=5120).
+constexpr int kRevFoldBatch = 4;
+
 template <typename IO, int L, int NW, bool GATE>
 __global__ __launch_bounds__(64 * NW, 4) void bwd_scan_kernel(BwdArgs args) {
     constexpr int TILE = L * NW;
@@ -718,7 +735,7 @@ __global__ __launch_bounds__(64 * NW, 4) void bwd_scan_kernel(BwdArgs args) {
                 have = true;
             } else if (!forced) {
                 publish_rev(recs, ci, 0, lane, agg_rec, recs.tag_agg);
-                have = rev_look_back<TILE>(args, recs, w2, ci, lane, rin);
+                have = rev_look_back<TILE, kRevFoldBatch>(args, recs, w2, ci, lane, rin);
             } else {
                 raise_give_up(args.ctrl, recs.give_up_word, lane);
             }
