@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 
 #include "libwkv.h"
@@ -42,6 +43,17 @@ int resolve_algo(wkv_algo algo, int64_t B, int64_t T, int64_t C) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (0 if unknown), looked up once per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cached[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
 
 // Chunk length when the caller passes 0: 256, or 512 for problems of fewer than 1024
 // tiles of 256, where the per-tile look-back dominates (B=8, T=1024, C=768 float32:
@@ -150,6 +162,9 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.n_chunks = (int)ceil_div(T, tile);
     const int64_t n_tiles = (int64_t)a.n_groups * a.n_chunks;
     if (n_tiles > INT_MAX) return WKV_EINVAL;
+    // a launch whose tiles can all be resident at once numbers them by workgroup index (B=8,
+    // T=1024, C=768 float32: 192 tiles, whose tickets would queue on one counter)
+    a.by_index = n_tiles <= (int64_t)cu_count() * wkv::fwd_chunked_resident_per_cu(io, tile, r != nullptr) ? 1 : 0;
     const ChunkLayout L = chunked_layout(B, T, C, tile);
     char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), kAlign));
     a.ctrl = reinterpret_cast<uint32_t*>(base);

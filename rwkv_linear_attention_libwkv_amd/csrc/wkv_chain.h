@@ -134,14 +134,17 @@ __device__ __forceinline__ int find_inclusive(const uint32_t* status, int n_chun
 // (nothing it could wait for is sure to exist) and flags the call with the mark a launch
 // that gave up leaves, one epoch behind the counter, which the workspace query reports.
 // Call with a wave-uniform ticket; every thread of the workgroup gets the same answer.
-__device__ __forceinline__ uint32_t remap_ticket(uint32_t ticket, uint32_t n_tiles, uint32_t* ctrl, bool& forced) {
-    if (ticket < n_tiles) return ticket;
-    forced = true;
+__device__ __forceinline__ void flag_stale_ticket(uint32_t* ctrl) {
     if (threadIdx.x == 0) {
         const uint32_t epoch = __hip_atomic_load(&ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctrl[kCtrlGiveUp], ((epoch - 1u) & kCtrlEpochMask) | kCtrlGiveUpMark, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+__device__ __forceinline__ uint32_t remap_ticket(uint32_t ticket, uint32_t n_tiles, uint32_t* ctrl, bool& forced) {
+    if (ticket < n_tiles) return ticket;
+    forced = true;
+    flag_stale_ticket(ctrl);
     return ticket % n_tiles;
 }
 

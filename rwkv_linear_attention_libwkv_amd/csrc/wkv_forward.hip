@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "wkv_device.h"
@@ -610,7 +611,7 @@ struct TileShared {
 // The tile after its k, v rows are loaded.  FAST: the wave's chunk is full and well
 // conditioned and stays in registers; otherwise the wave walks its rows in memory with
 // the exact log-sum-exp recurrence.  Both instantiations pass the same two barriers.
-template <typename IO, int L, int NW, bool FAST, bool GATE>
+template <typename IO, int L, int NW, bool FAST, bool GATE, bool BYIDX>
 __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Chunk<IO, L>::kStashRows>& sh,
                                           const TileRecs& recs, const WaveRows& rows, Chunk<IO, L>& chunk,
                                           const Chan& ch, float R, int lane, int wid, int ci, int bi, int c,
@@ -636,6 +637,12 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
 
     // ---- wave 0: tile aggregate, look-back, publish ----
     if (wid == 0) {
+        // numbered by index: a ticket past the launch's tiles shows a counter that was not zero
+        if (BYIDX && (uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket) >=
+                         (uint32_t)args.n_groups * (uint32_t)args.n_chunks) {
+            forced = true;
+            flag_stale_ticket(args.ctrl);
+        }
         // the previous tile's inclusive record, read first: when it is complete, as it usually is
         // by the time the tile has its aggregate, the look-back is skipped
         uint64_t pv[3];
@@ -728,7 +735,7 @@ __device__ __forceinline__ void tile_body(const FwdArgs& args, TileShared<NW, Ch
     }
 }
 
-template <typename IO, int L, int NW, bool GATE>
+template <typename IO, int L, int NW, bool GATE, bool BYIDX>
 __global__ __launch_bounds__(64 * NW, NW >= 2 ? 4 : 1) void fwd_chunked_kernel(FwdArgs args) {
     constexpr int TILE = L * NW;
     const int lane = threadIdx.x & 63;
@@ -737,12 +744,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 2 ? 4 : 1) void fwd_chunked_kernel(F
     __shared__ TileShared<NW, Chunk<IO, L>::kStashRows> sh;
 
     // Tiles are numbered in the order workgroups start, so every tile this one waits on
-    // has already started and publishes its aggregate without waiting for anything.
-    if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
-    __syncthreads();
+    // has already started and publishes its aggregate without waiting for anything.  When
+    // every tile of the launch can be resident at once, the workgroup index numbers them
+    // instead and the loads start without waiting for a ticket (all tiles then run
+    // together, and the ticket, taken after the loads, only checks the counter).
+    const uint32_t n_tiles = (uint32_t)args.n_groups * (uint32_t)args.n_chunks;
     bool forced = false;
-    const int ticket = (int)remap_ticket((uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket),
-                                         (uint32_t)args.n_groups * (uint32_t)args.n_chunks, args.ctrl, forced);
+    int ticket;
+    if constexpr (BYIDX) {
+        ticket = (int)blockIdx.x;
+    } else {
+        if (threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
+        __syncthreads();
+        ticket = (int)remap_ticket((uint32_t)__builtin_amdgcn_readfirstlane(sh.ticket), n_tiles, args.ctrl, forced);
+    }
     const int g = ticket % args.n_groups;
     const int ci = ticket / args.n_groups;
     const int bi = g / args.groups_per_row;
@@ -769,6 +784,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 2 ? 4 : 1) void fwd_chunked_kernel(F
     }
     Chunk<IO, L> chunk;
     chunk.load(rows, nv, cvalid);
+    if (BYIDX && threadIdx.x == 0) sh.ticket = (int)atomicAdd(&args.ctrl[kCtrlTicket], 1u);
 
     // read after the loads are issued; constant during the launch
     const uint32_t epoch = __builtin_amdgcn_readfirstlane(args.ctrl[kCtrlEpoch]);
@@ -790,15 +806,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 2 ? 4 : 1) void fwd_chunked_kernel(F
     // sequence (and any ill-conditioned chunk) walks its rows exactly
     const size_t seq_off = ((size_t)bi * T * C + c_grp) * sizeof(IO);  // time step 0 of this group
     if (__all(chunk_fast_ok(ch, kmax, kmin)) && nv == L)
-        tile_body<IO, L, NW, true, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
+        tile_body<IO, L, NW, true, GATE, BYIDX>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
                                          t_tile, tile_len, g, forced, seq_off);
     else
-        tile_body<IO, L, NW, false, GATE>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
+        tile_body<IO, L, NW, false, GATE, BYIDX>(args, sh, recs, rows, chunk, ch, R, lane, wid, ci, bi, c, cvalid, nv,
                                           t_tile, tile_len, g, forced, seq_off);
 
     // ---- launch bookkeeping: the last workgroup to finish prepares the next launch ----
     __syncthreads();
-    if (threadIdx.x == 0) finish_tile(args.ctrl, (uint32_t)args.n_groups * (uint32_t)args.n_chunks, epoch, false);
+    if (threadIdx.x == 0) finish_tile(args.ctrl, n_tiles, epoch, false);
 }
 
 // One control word of a workspace set from the stream (no memset: callers may capture it).
@@ -846,15 +862,72 @@ hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch_seq_t<float>(a, s) : launch_seq_t<uint16_t>(a, s);
 }
 
-template <typename IO, int NW>
-static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
+template <typename IO, int NW, bool BYIDX>
+static void launch_chunked_g(const FwdArgs& a, hipStream_t s) {
     constexpr int L = chunk_tokens<IO>();
     const long n_tiles = (long)a.n_groups * a.n_chunks;
     if (a.r)
-        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, true>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, true, BYIDX>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s,
+                           a);
     else
-        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, false>), dim3((unsigned)n_tiles), dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((fwd_chunked_kernel<IO, L, NW, false, BYIDX>), dim3((unsigned)n_tiles), dim3(64 * NW), 0,
+                           s, a);
+}
+
+template <typename IO, int NW>
+static hipError_t launch_chunked_t(const FwdArgs& a, hipStream_t s) {
+    if (a.by_index)
+        launch_chunked_g<IO, NW, true>(a, s);
+    else
+        launch_chunked_g<IO, NW, false>(a, s);
     return hipGetLastError();
+}
+
+// Workgroups of the index-numbered kernel that one compute unit holds at once (0 if unknown),
+// looked up once per instantiation.
+template <typename IO, int NW>
+static int resident_t(bool gate) {
+    constexpr int L = chunk_tokens<IO>();
+    static std::atomic<int> cached[2];
+    int n = cached[gate].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    hipError_t e = gate ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_chunked_kernel<IO, L, NW, true, true>,
+                                                                       64 * NW, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_chunked_kernel<IO, L, NW, false, true>,
+                                                                       64 * NW, 0);
+    if (e != hipSuccess || n <= 0) return 0;
+    cached[gate].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+template <typename IO>
+static int resident_n(int tile, bool gate) {
+    constexpr int L = chunk_tokens<IO>();
+    if constexpr (L == 64) {
+        switch (tile) {
+            case 64: return resident_t<IO, 1>(gate);
+            case 128: return resident_t<IO, 2>(gate);
+            case 256: return resident_t<IO, 4>(gate);
+            case 512: return resident_t<IO, 8>(gate);
+        }
+    } else {
+        switch (tile) {
+            case 64: return resident_t<IO, 2>(gate);
+            case 128: return resident_t<IO, 4>(gate);
+            case 256: return resident_t<IO, 8>(gate);
+            case 512: return resident_t<IO, 16>(gate);
+        }
+    }
+    return 0;
+}
+
+int fwd_chunked_resident_per_cu(int io, int tile, bool gate) {
+    switch (io) {
+        case kIoF32: return resident_n<float>(tile, gate);
+        case kIoBf16: return resident_n<uint16_t>(tile, gate);
+        case kIoBf16Pair: return resident_n<Bf16Pair>(tile, gate);
+    }
+    return 0;
 }
 
 // Tile = NW waves x chunk_tokens tokens, 64 channels; at most 16 waves (1024 threads).

@@ -47,6 +47,8 @@ struct FwdArgs {
     int groups_per_row;  // ceil(C / 64)
     int n_groups;        // B * groups_per_row
     int n_chunks;        // ceil(T / tile)
+    int by_index;        // 1: every tile of the launch can be resident at once, and tiles are
+                         //   numbered by workgroup index instead of a ticket (chunked only)
 };
 
 // How the chunked kernel moves k, v, y (and r): float32 rows; bfloat16 rows at 2 bytes per
@@ -58,6 +60,8 @@ enum IoMode { kIoF32 = 0, kIoBf16 = 1, kIoBf16Pair = 2 };
 hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s);
 // tile: 64, 128, 256 or 512 time steps per workgroup.
 hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s);
+// Workgroups of the index-numbered chunked kernel one compute unit holds at once (0 if unknown).
+int fwd_chunked_resident_per_cu(int io, int tile, bool gate);
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t s);
 hipError_t launch_copy_state(const float* ia, const float* ib, const float* ip, float* oa,

@@ -287,16 +287,18 @@ def test_workspace_epoch_counts_chunked_calls():
     assert libwkv.workspace_query(ws) == (0, 3)
 
 
-def test_stale_ticket_counter_is_flagged():
+@pytest.mark.parametrize("T", [900, 20000])
+def test_stale_ticket_counter_is_flagged(T):
     """A workspace whose ticket counter was not zero (here: set past every tile) makes the chunked
-    forward flag the call; every tile is still computed once (ticket mod the number of tiles, on
-    the path that waits for nothing), so y matches the oracle, and the launch's last workgroup
-    leaves the counters ready for the next call."""
-    inp = special(B=2, T=900, C=128)
+    forward flag the call; every tile is still computed once (ticket mod the number of tiles, or
+    the workgroup index, on the path that waits for nothing), so y matches the oracle, and the
+    launch's last workgroup leaves the counters ready for the next call.  T = 900: 32 tiles, fewer
+    than the compute units, numbered by workgroup index; T = 20000: 628 tiles, numbered by ticket."""
+    inp = special(B=2, T=T, C=128)
     dev = to_device(inp)
     k = dev["k"]
     y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
-    ws = libwkv.new_workspace(2, 900, 128, k.dtype, "chunked", 128)
+    ws = libwkv.new_workspace(2, T, 128, k.dtype, "chunked", 128)
     ws.view(torch.int32)[0] = (1 << 30) + 5  # the ticket counter (first word of the control block)
     y = torch.full_like(k, 7.0)
     libwkv.wkv_forward(dev["w"], dev["u"], k, dev["v"], algo="chunked", chunk_len=128, y=y, workspace=ws)
