@@ -28,9 +28,12 @@ def fwd_inputs(B, T, C, dtype="f32", seed=3, **kw):
 
 @pytest.mark.parametrize("dtype,B,T,C,chunk", [("f32", 2, 3000, 130, 256), ("f32", 1, 5000, 64, 128),
                                                ("bf16", 2, 4100, 128, 512), ("bf16", 1, 3000, 67, 256),
-                                               ("f32", 3, 700, 200, 64)])
+                                               ("f32", 3, 700, 200, 64), ("f32", 4, 40000, 128, 128),
+                                               ("bf16", 2, 40000, 256, 512)])
 def test_forward_forced(dtype, B, T, C, chunk):
-    """Every tile rebuilds its entering state; the next call on the workspace is back on the usual path."""
+    """Every tile rebuilds its entering state; the next call on the workspace is back on the usual path.
+    The first five launches fit on the GPU at once (tiles numbered by workgroup index); the last two
+    have 2504 and 632 tiles, more than fit, and take tickets."""
     inp = fwd_inputs(B, T, C, dtype, seed=B + T + C, k_std=1.5)
     dev = to_device(inp)
     y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], return_scale=True)
