@@ -244,6 +244,11 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const fl
     size_t fps = sps / 4;
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(base);
     if (!saved) {
+        // the forward's own tile: 512 for bfloat16 row pairs (eight waves of 64 tokens), else the
+        // default; its carve-up fits in the part of the workspace sized at the default tile
+        const int io_f = chunk_io(dt, C, k, v, k);
+        const int ftile = io_f == wkv::kIoBf16Pair ? 2 * kDefaultTile : L.fwd_tile;
+        const ChunkLayout FL = chunked_layout(B, T, C, ftile);
         wkv::FwdArgs f{};
         f.w = w;
         f.u = u;
@@ -255,15 +260,17 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const fl
         f.C = (int)C;
         f.groups_per_row = groups_per_row;
         f.n_groups = (int)n_groups;
-        f.n_chunks = (int)ceil_div(T, L.fwd_tile);
+        f.n_chunks = (int)ceil_div(T, ftile);
+        f.by_index = n_groups * f.n_chunks <= (int64_t)cu_count() * wkv::fwd_chunked_resident_per_cu(io_f, ftile, false)
+                         ? 1
+                         : 0;
         f.ctrl = ctrl;
-        f.status = reinterpret_cast<uint32_t*>(base + L.fwd.off_status);
-        f.recs = base + L.fwd.off_recs;
+        f.status = reinterpret_cast<uint32_t*>(base + FL.off_status);
+        f.recs = base + FL.off_recs;
         f.dump_a = planes + 2 * ps;
         f.dump_b = planes + 3 * ps;
         f.dump_p = planes + 4 * ps;
-        if (wkv::launch_fwd_chunked(f, chunk_io(dt, C, k, v, k), L.fwd_tile, stream) != hipSuccess)
-            return WKV_EHIP;
+        if (wkv::launch_fwd_chunked(f, io_f, ftile, stream) != hipSuccess) return WKV_EHIP;
         fw = planes + 2 * ps;
         fps = ps;
     }
