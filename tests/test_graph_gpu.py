@@ -227,3 +227,54 @@ def test_token_shift_and_backward():
             st[n].copy_(sets[i][n])
 
     replay_and_check(graph, load, lambda: [out, gx, gmu, gprev], expected)
+
+
+FIRST_CALL_CAPTURED = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+from rwkv_linear_attention_libwkv_amd import libwkv, workloads
+
+# the process's first call into the library is made under capture: the per-device lookups the
+# chunked forward makes on its first launch (compute units, resident workgroups) happen inside it
+inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=2, T=1500, C=128, seed=4))
+t = lambda a: torch.from_numpy(a).cuda()
+w, u, k, v = t(inp["w"]), t(inp["u"]), t(inp["k"]), t(inp["v"])
+y = torch.empty_like(k)
+ws = libwkv.new_workspace(2, 1500, 128, torch.float32, "chunked", 256)
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    lib = libwkv.lib
+    st = lib.wkv_forward_ex(2, 1500, 128, 0, w.data_ptr(), u.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            y.data_ptr(), ws.data_ptr(), ws.numel(), 2, 256, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, st
+torch.cuda.synchronize()
+outs = []
+for _ in range(3):
+    y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    outs.append(y.clone())
+ref = libwkv.wkv_forward(w, u, k, v, algo="chunked", chunk_len=256)
+torch.cuda.synchronize()
+assert all(torch.equal(o, ref) for o in outs)
+print("first call captured: ok", flush=True)
+"""
+
+
+def test_first_call_under_capture(tmp_path):
+    """In a fresh process whose first call into the library is captured, the capture succeeds and
+    every replay equals the eager call bit for bit (a child process, so that nothing earlier in
+    this one has made the first launch)."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "first_call.py"
+    script.write_text(FIRST_CALL_CAPTURED)
+    r = subprocess.run([sys.executable, str(script), root], capture_output=True, text=True, timeout=240)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0 and "first call captured: ok" in r.stdout
