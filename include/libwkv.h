@@ -77,7 +77,7 @@ typedef enum wkv_dtype {
 
 /* How wkv_forward_ex computes the time recurrence. */
 typedef enum wkv_algo {
-    WKV_ALGO_AUTO = 0,    /* pick by the number of lanes B*C versus T */
+    WKV_ALGO_AUTO = 0,    /* chunked, except SEQ for T <= 64 (and B <= 65535) */
     WKV_ALGO_SEQ = 1,     /* one thread walks all of T for its channels */
     WKV_ALGO_CHUNKED = 2  /* T split into chunks, single-pass chained scan */
 } wkv_algo;
@@ -167,8 +167,9 @@ wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, wkv_dtype dt,
  * (hipGetSymbolAddress, with that device current) and clears its launch
  * counters with a small kernel on `stream`.  Same kernels and results as
  * wkv_forward.  A problem whose workspace (wkv_forward_workspace_bytes with
- * WKV_ALGO_AUTO, chunk 0) exceeds 32 MiB gives WKV_EWORKSPACE, before any
- * launch.  All calls on one GPU share that GPU's array, which keeps the last
+ * WKV_ALGO_AUTO, chunk 0) exceeds 32 MiB runs the sequential algorithm (as
+ * wkv_forward_ex with WKV_ALGO_SEQ, which needs no workspace), or, with
+ * B > 65535 (beyond its grid), gives WKV_EWORKSPACE before any launch.  All calls on one GPU share that GPU's array, which keeps the last
  * call's records: calls that may overlap in time on the same GPU (other
  * streams, other host threads) race and must not be made.  Other arguments
  * and errors as wkv_forward.

@@ -62,7 +62,12 @@ extern "C" wkv_status wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, wkv_d
                                           hipStream_t stream) {
     const size_t need = wkv_forward_workspace_bytes(B, T, C, dt, WKV_ALGO_AUTO, 0);
     if (need == (size_t)-1) return dt == WKV_F32 || dt == WKV_BF16 ? WKV_EINVAL : WKV_EDTYPE;
-    if (need > kScratchBytes) return WKV_EWORKSPACE;
+    if (need > kScratchBytes) {
+        // beyond the array: the sequential algorithm, which needs no workspace, when its grid
+        // can hold the batch rows
+        if (B > 65535) return WKV_EWORKSPACE;
+        return wkv_forward_ex(B, T, C, dt, w, u, k, v, y, nullptr, 0, WKV_ALGO_SEQ, 0, stream);
+    }
     if (need == 0)  // empty problem or sequential algorithm: no workspace at all
         return wkv_forward(B, T, C, dt, w, u, k, v, y, nullptr, 0, stream);
     if (!w || !u || !k || !v || !y) return WKV_EINVAL;

@@ -33,7 +33,7 @@ def test_wide_rows_forward(dtype, C):
                                return_scale=True)
     dev = to_device(inp)
     del inp
-    for algo, cl in (("auto", 0), ("chunked", 128)):  # auto walks T: B*C is over 2^19 lanes
+    for algo, cl in (("auto", 0), ("seq", 0), ("chunked", 128)):  # auto: the chunked scan at its default tile
         y = run_forward(dev, algo, cl)
         err = scaled_error(host(y[:, :, torch.from_numpy(cs).cuda()]), ref, scale)
         print(f"  wide rows {dtype} C={C} {algo} {cl}: {err:.2e}", flush=True)

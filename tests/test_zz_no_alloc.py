@@ -46,12 +46,30 @@ def test_noalloc_matches_forward(first, second):
 
 
 def test_noalloc_rejects_problems_beyond_the_array():
-    """More than 32 MiB of workspace: WKV_EWORKSPACE before any launch (dummy pointers)."""
-    B, T, C = 4, 65536, 5120
+    """More than 32 MiB of workspace and more batch rows than the sequential kernel's grid holds:
+    WKV_EWORKSPACE before any launch (dummy pointers)."""
+    B, T, C = 65536, 4096, 64
     need = libwkv.wkv_forward_workspace_bytes(B, T, C, torch.bfloat16)
     assert need > SCRATCH_BYTES
     p = ctypes.c_void_p(0x1000)
     assert libwkv.lib.wkv_forward_noalloc(B, T, C, libwkv.WKV_BF16, p, p, p, p, p, None) == libwkv.WKV_EWORKSPACE
+
+
+def test_noalloc_beyond_the_array_runs_sequentially():
+    """More than 32 MiB of workspace with B <= 65535: the sequential algorithm, bit for bit what
+    wkv_forward gives with algo="seq", and within the tolerance of the oracle on sampled rows."""
+    B, T, C = 512, 512, 768
+    assert libwkv.wkv_forward_workspace_bytes(B, T, C, torch.float32) > SCRATCH_BYTES
+    inp = workloads.forward_inputs(workloads.FWD_SMALL.with_(B=B, T=T, C=C, seed=12))
+    dev = to_device(inp)
+    y = torch.empty_like(dev["k"])
+    assert call_noalloc(dev, y) == libwkv.WKV_OK
+    y_seq = libwkv.wkv_forward(dev["w"], dev["u"], dev["k"], dev["v"], algo="seq")
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_seq)
+    rows = [0, 1, 255, 511]
+    y_ref, s_ref = wkv_recurrent(inp["w"], inp["u"], inp["k"][rows], inp["v"][rows], return_scale=True)
+    assert scaled_error(host(y[rows]), y_ref, s_ref) <= TOL["f32"]
 
 
 def test_noalloc_sequential_and_empty():
