@@ -145,15 +145,14 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, wkv_dtype dt, const flo
     a.T = (int)T;
     a.C = (int)C;
 
-    const int dtype = dt == WKV_F32 ? 0 : 1;
     const int resolved = resolve_algo(algo, B, T, C);
-    if (resolved == WKV_ALGO_SEQ) {
-        if (B > 65535) return WKV_EINVAL;  // batch rows are grid.y
-        return wkv::launch_fwd_seq(a, dtype, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
-    }
-
     int io = chunk_io(dt, C, k, v, y);
     if (io == wkv::kIoBf16Pair && r && !aligned(r, 4)) io = wkv::kIoBf16;
+    if (resolved == WKV_ALGO_SEQ) {
+        if (B > 65535) return WKV_EINVAL;  // batch rows are grid.y
+        return wkv::launch_fwd_seq(a, io, stream) == hipSuccess ? WKV_OK : WKV_EHIP;
+    }
+
     // bfloat16 row pairs hold 64 tokens per wave, so their tile of eight waves is 512 tokens
     // (B=1, T=65536, C=5120: 406-412 us against 414-418 us at 256; B=8, T=8192, C=2048:
     // 164-168 us against 170-172 us); it needs no more workspace than default_tile's

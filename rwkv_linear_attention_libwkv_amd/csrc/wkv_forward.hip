@@ -336,18 +336,25 @@ constexpr int chunk_tokens() { return kPair<IO> ? 64 : 32; }
 // Sequential kernel
 // ----------------------------------------------------------------------------
 
-// grid: x covers the channels of one batch row, y is the batch row.
+// grid: x covers the channels of one batch row, y is the batch row.  bfloat16 row pairs: a
+// wave's 64 channels move as two rows per instruction, as in the chunked kernel (every lane
+// of the wave then takes part in the exchanges; lanes past C only skip their loads and stores).
 template <typename IO, int L, bool GATE>
 __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
     const int C = args.C, T = args.T;
     const int bi = blockIdx.y;
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= C) return;
+    const int lane = threadIdx.x & 63;
+    const int c_grp = blockIdx.x * 256 + (threadIdx.x & ~63);
+    const int c = c_grp + (kPair<IO> ? pair_channel(lane) : lane);
+    const bool cvalid = c < C;
+    if (kPair<IO> ? c_grp >= C : !cvalid) return;  // pairs: only whole waves leave
 
-    const Chan ch = make_chan(args.w[c], args.u[c]);
-    const size_t si = (size_t)bi * C + c;
-    Carry st = args.sin_a ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si]) : empty_carry();
-    const size_t row_elems = (size_t)bi * T * C;
+    const int cw = cvalid ? c : 0;
+    const Chan ch = make_chan(args.w[cw], args.u[cw]);
+    const size_t si = (size_t)bi * C + cw;
+    Carry st = (args.sin_a && cvalid) ? carry_from_abi(args.sin_a[si], args.sin_b[si], args.sin_p[si])
+                                      : empty_carry();
+    const size_t row_elems = (size_t)bi * T * C + c_grp;
 
     for (int t0 = 0; t0 < T; t0 += L) {
         const int nv = min(L, T - t0);
@@ -357,10 +364,13 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         w.v = make_rsrc(static_cast<const char*>(args.v) + off);
         w.y = make_rsrc(static_cast<char*>(args.y) + off);
         if constexpr (GATE) w.r = make_rsrc(static_cast<const char*>(args.r) + off);
-        w.lane_off = (uint32_t)(c * sizeof(IO));
+        w.lane_off = (uint32_t)((c - c_grp) * sizeof(IO));
         w.row_bytes = (uint32_t)(C * sizeof(IO));
+        w.pair_off = (uint32_t)((lane & 31) * 4) + (uint32_t)(lane >> 5) * w.row_bytes;
+        w.upper = (uint32_t)(lane >> 5);
+        w.partner = (uint32_t)((lane ^ 32) << 2);
         Chunk<IO, L> chunk;
-        chunk.load(w, nv, true);
+        chunk.load(w, nv, cvalid);
         float kmax, kmin;
         chunk.range(kmax, kmin);
         st = normalize(st);
@@ -369,16 +379,18 @@ __global__ __launch_bounds__(256) void fwd_seq_kernel(FwdArgs args) {
         const bool ok = nv == L && chunk_fast_ok(ch, kmax, kmin) && (st.p - (double)R <= (double)kSpan);
         if (__all(ok)) {
             chunk.weights(R);
-            if constexpr (GATE)
-                st = chunk.outputs_gated(ch, st, R, w, true);
-            else
+            if constexpr (GATE) {
+                if constexpr (kPair<IO>) chunk.prefetch_gate(w, cvalid);
+                st = chunk.outputs_gated(ch, st, R, w, cvalid);
+            } else {
                 st = chunk.outputs(ch, st, R);
-            chunk.store(w, true);
+            }
+            chunk.store(w, cvalid);
         } else {
-            lse_walk<IO, true, GATE>(ch, st, w, nv, true, true);
+            lse_walk<IO, true, GATE>(ch, st, w, nv, cvalid, cvalid);
         }
     }
-    if (args.sout_a) carry_to_abi(st, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
+    if (args.sout_a && cvalid) carry_to_abi(st, args.sout_a[si], args.sout_b[si], args.sout_p[si]);
 }
 
 // ----------------------------------------------------------------------------
@@ -850,16 +862,22 @@ __global__ void copy_state_kernel(const float* __restrict__ ia, const float* __r
 
 template <typename IO>
 static hipError_t launch_seq_t(const FwdArgs& a, hipStream_t s) {
+    constexpr int L = 32;  // tokens per chunk (bf16 row pairs: 16 packed words of k and of v)
     const long blocks = (a.C + 255) / 256;
     if (a.r)
-        hipLaunchKernelGGL((fwd_seq_kernel<IO, 32, true>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_seq_kernel<IO, L, true>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((fwd_seq_kernel<IO, 32, false>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_seq_kernel<IO, L, false>), dim3((unsigned)blocks, (unsigned)a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_seq_t<float>(a, s) : launch_seq_t<uint16_t>(a, s);
+hipError_t launch_fwd_seq(const FwdArgs& a, int io, hipStream_t s) {
+    switch (io) {
+        case kIoF32: return launch_seq_t<float>(a, s);
+        case kIoBf16: return launch_seq_t<uint16_t>(a, s);
+        case kIoBf16Pair: return launch_seq_t<Bf16Pair>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename IO, int NW, bool BYIDX>

@@ -56,8 +56,8 @@ struct FwdArgs {
 // runs one channel per lane, 64 channels per group.
 enum IoMode { kIoF32 = 0, kIoBf16 = 1, kIoBf16Pair = 2 };
 
-// dtype: 0 = float32, 1 = bfloat16.
-hipError_t launch_fwd_seq(const FwdArgs& a, int dtype, hipStream_t s);
+// io: an IoMode (below), as for the chunked kernel.
+hipError_t launch_fwd_seq(const FwdArgs& a, int io, hipStream_t s);
 // tile: 64, 128, 256 or 512 time steps per workgroup.
 hipError_t launch_fwd_chunked(const FwdArgs& a, int io, int tile, hipStream_t s);
 // Workgroups of the index-numbered chunked kernel one compute unit holds at once (0 if unknown).
