@@ -106,9 +106,14 @@ def test_workspace_query():
     a = q(8, 8192, 2048, F32, 2, 0)
     assert a > 0 and a == q(8, 8192, 2048, BF16, 2, 0)
     assert q(8, 8192, 2048, F32, 2, 64) > q(8, 8192, 2048, F32, 2, 256)
-    # AUTO picks the chunked scan for long T with few lanes, the walk for short T
+    # AUTO picks the chunked scan for every T over 64, whatever the number of lanes, and the
+    # sequential walk (no workspace) for T up to 64 unless B is beyond its grid (65535 rows)
     assert q(1, 65536, 5120, BF16, 0, 0) > 0
     assert q(1, 64, 64, F32, 0, 0) == 0
+    assert q(8192, 64, 1024, F32, 0, 0) == 0
+    assert q(8192, 65, 1024, F32, 0, 0) == q(8192, 65, 1024, F32, 2, 0) > 0
+    assert q(1024, 1024, 768, BF16, 0, 0) == q(1024, 1024, 768, BF16, 2, 0) > 0
+    assert q(65536, 64, 64, F32, 0, 0) == q(65536, 64, 64, F32, 2, 0) > 0
 
 
 def test_workspace_diagnostics_argument_checks():
