@@ -141,7 +141,8 @@ def _dtype_code(t: torch.dtype) -> int:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the argtypes declare c_void_p, so ctypes converts the integer address itself
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
@@ -174,14 +175,14 @@ def _gpu_args(**tensors):
     """Every given tensor (None entries skipped) is a contiguous tensor on the current GPU.  The
     kernels take raw device pointers: a host or other-device pointer would fault the GPU, so it
     is refused here."""
-    dev = None
+    cur = -1
     for name, t in tensors.items():
         if t is None:
             continue
         _need(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a GPU tensor")
-        if dev is None:
-            dev = torch.device("cuda", torch.cuda.current_device())
-        _need(t.device == dev, f"{name} is on {t.device}, the launch goes to {dev}")
+        if cur < 0:
+            cur = torch.cuda.current_device()
+        _need(t.get_device() == cur, f"{name} is on {t.device}, the launch goes to cuda:{cur}")
         _need(t.is_contiguous(), f"{name} must be contiguous")
 
 
